@@ -1,0 +1,234 @@
+"""Plain fp64 CPU reference for the masked multi-head attention forward.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the package smoke check and the
+CPU-baseline leg of the benchmark are the only callers. The GPU library never
+imports, links or runs anything here, and nothing here imports the GPU package.
+
+The arithmetic lives in ``mha_oracle.c`` (built into ``liboracle.so`` by
+``oracle/build.py``); this module only marshals numpy arrays into it. Every
+array handed in is float64 (inputs are the same dtype-rounded values the GPU
+receives, widened exactly), int32 for padding lengths.
+
+Parity status: every function here is pinned by tests that do not reuse its
+code (brute force in exact decimal arithmetic, library special cases, closed
+forms and invariants) -- none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+CAUSAL, PADDING, ADDITIVE = 1, 2, 4
+FLAG_FULLY_MASKED_ROW, FLAG_NONFINITE, FLAG_BAD_LENGTH = 1, 2, 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_lp = ctypes.POINTER(ctypes.c_int64)
+_bp = ctypes.POINTER(ctypes.c_uint8)
+_i, _u, _d, _l = ctypes.c_int, ctypes.c_uint, ctypes.c_double, ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "oracle_threads": ([], _i),
+        "oracle_set_threads": ([_i], None),
+        "oracle_mha_fwd": ([_dp, _dp, _dp, _ip, _dp, _u, _i, _i, _i, _i, _i, _d, _dp], ctypes.c_uint32),
+        "oracle_mha_rows": ([_dp, _dp, _dp, _ip, _dp, _u, _i, _i, _i, _i, _i, _d, _lp, _l, _dp],
+                            ctypes.c_uint32),
+        "oracle_probs_row": ([_dp, _dp, _ip, _dp, _u, _i, _i, _i, _i, _i, _d, _i, _i, _i, _dp],
+                             ctypes.c_uint32),
+        "oracle_layernorm": ([_dp, _dp, _dp, _d, _l, _i, _dp], None),
+        "oracle_prenorm_rows": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _dp, _i, _i, _i, _i,
+                                 _i, _d, _lp, _l, _dp], ctypes.c_uint32),
+        "oracle_prenorm_cross_fwd": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _dp, _i, _i, _i,
+                                      _i, _i, _d, _dp], ctypes.c_uint32),
+        "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _bp], None),
+        "oracle_unmasked_pairs": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
+        "oracle_tile_counts": ([_ip, _dp, _u, _i, _i, _i, _i, _i, _i, _lp], None),
+        "oracle_fully_masked_rows": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _ptr(a, typ):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+def _mask_args(kind, lens, add, B, Lq, Lk):
+    if kind & PADDING:
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        if lens.shape != (B,):
+            raise ValueError("lens must have shape [B]")
+    else:
+        lens = None
+    if kind & ADDITIVE:
+        add = _f64(add, (B, 1, Lq, Lk))
+    else:
+        add = None
+    return lens, add
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def mha_fwd(q, k, v, kind=0, lens=None, add=None, scale=None):
+    """Full forward. q [B,H,Lq,D], k/v [B,H,Lk,D] -> (out [B,H,Lq,D], flags)."""
+    q = _f64(q)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    k = _f64(k, (B, H, Lk, D))
+    v = _f64(v, (B, H, Lk, D))
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((B, H, Lq, D), np.float64)
+    f = _load().oracle_mha_fwd(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip),
+                               _ptr(add, _dp), kind, B, H, Lq, Lk, D, scale, _ptr(out, _dp))
+    return out, int(f)
+
+
+def mha_rows(q, k, v, rows, kind=0, lens=None, add=None, scale=None):
+    """Selected rows; rows is an int array [n,3] of (b, h, i). -> (out [n,D], flags)."""
+    q = _f64(q)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    k = _f64(k, (B, H, Lk, D))
+    v = _f64(v, (B, H, Lk, D))
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], D), np.float64)
+    f = _load().oracle_mha_rows(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip),
+                                _ptr(add, _dp), kind, B, H, Lq, Lk, D, scale,
+                                _ptr(rows, _lp), rows.shape[0], _ptr(out, _dp))
+    return out, int(f)
+
+
+def probs_row(q, k, b, h, i, kind=0, lens=None, add=None, scale=None):
+    """Softmax weights of one row -> (p [Lk], flags)."""
+    q = _f64(q)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    k = _f64(k, (B, H, Lk, D))
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    p = np.empty(Lk, np.float64)
+    f = _load().oracle_probs_row(_ptr(q, _dp), _ptr(k, _dp), _ptr(lens, _ip), _ptr(add, _dp),
+                                 kind, B, H, Lq, Lk, D, scale, b, h, i, _ptr(p, _dp))
+    return p, int(f)
+
+
+def layernorm(x, gamma, beta, eps):
+    """Per-token LayerNorm over the last axis of x."""
+    x = _f64(x)
+    F = x.shape[-1]
+    gamma = _f64(gamma, (F,))
+    beta = _f64(beta, (F,))
+    y = np.empty_like(x)
+    _load().oracle_layernorm(_ptr(x, _dp), _ptr(gamma, _dp), _ptr(beta, _dp), float(eps),
+                             x.size // F, F, _ptr(y, _dp))
+    return y
+
+
+def _prenorm_common(x, k, v, gamma, beta, residual, kind, lens, add, scale):
+    x = _f64(x)
+    B, Lq, F = x.shape
+    _, H, Lk, D = k.shape
+    if H * D != F:
+        raise ValueError("x feature width must equal H*D")
+    k = _f64(k, (B, H, Lk, D))
+    v = _f64(v, (B, H, Lk, D))
+    gamma = _f64(gamma, (F,))
+    beta = _f64(beta, (F,))
+    residual = _f64(residual, (B, Lq, F)) if residual is not None else None
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    return x, k, v, gamma, beta, residual, lens, add, scale, (B, H, Lq, Lk, D)
+
+
+def prenorm_cross_fwd(x, k, v, gamma, beta, eps, residual=None, kind=0, lens=None, add=None,
+                      scale=None):
+    """Full pre-LN cross-attention. x [B,Lq,H*D] -> (out [B,Lq,H*D], flags)."""
+    x, k, v, gamma, beta, residual, lens, add, scale, (B, H, Lq, Lk, D) = _prenorm_common(
+        x, k, v, gamma, beta, residual, kind, lens, add, scale)
+    out = np.empty((B, Lq, H * D), np.float64)
+    f = _load().oracle_prenorm_cross_fwd(
+        _ptr(x, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip), _ptr(add, _dp), kind,
+        _ptr(gamma, _dp), _ptr(beta, _dp), float(eps), _ptr(residual, _dp), B, H, Lq, Lk, D,
+        scale, _ptr(out, _dp))
+    return out, int(f)
+
+
+def prenorm_rows(x, k, v, gamma, beta, eps, rows, residual=None, kind=0, lens=None, add=None,
+                 scale=None):
+    """Selected rows (b, i, h) of the pre-LN cross-attention -> (out [n,D], flags)."""
+    x, k, v, gamma, beta, residual, lens, add, scale, (B, H, Lq, Lk, D) = _prenorm_common(
+        x, k, v, gamma, beta, residual, kind, lens, add, scale)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], D), np.float64)
+    f = _load().oracle_prenorm_rows(
+        _ptr(x, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip), _ptr(add, _dp), kind,
+        _ptr(gamma, _dp), _ptr(beta, _dp), float(eps), _ptr(residual, _dp), B, H, Lq, Lk, D,
+        scale, _ptr(rows, _lp), rows.shape[0], _ptr(out, _dp))
+    return out, int(f)
+
+
+def mask_decisions(kind, B, Lq, Lk, lens=None, add=None):
+    """uint8 [B,Lq,Lk], 1 where the pair is masked."""
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    dec = np.empty((B, Lq, Lk), np.uint8)
+    _load().oracle_mask_decisions(_ptr(lens, _ip), _ptr(add, _dp), kind, B, Lq, Lk,
+                                  _ptr(dec, _bp))
+    return dec
+
+
+def unmasked_pairs(kind, B, H, Lq, Lk, lens=None, add=None) -> int:
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    return int(_load().oracle_unmasked_pairs(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H, Lq, Lk))
+
+
+def tile_counts(kind, B, H, Lq, Lk, rm, bn, lens=None, add=None):
+    """(computed, skipped) tiles of rm rows x bn keys, summed over b and h."""
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    c = np.zeros(2, np.int64)
+    _load().oracle_tile_counts(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H, Lq, Lk, rm, bn,
+                               _ptr(c, _lp))
+    return int(c[0]), int(c[1])
+
+
+def fully_masked_rows(kind, B, H, Lq, Lk, lens=None, add=None) -> int:
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    return int(_load().oracle_fully_masked_rows(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H,
+                                                Lq, Lk))

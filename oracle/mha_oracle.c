@@ -1,0 +1,347 @@
+/*
+ * mha_oracle.c -- plain, slow, fp64 CPU reference for the masked multi-head
+ * attention forward and its pre-LayerNorm cross-attention variant.
+ *
+ * TEST INFRASTRUCTURE. Only the test-suite, the package smoke check and the
+ * CPU-baseline leg of the benchmark load this library. The GPU library never
+ * links it, calls it or shares code with it.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [MMHA]  "masked multi head attention" CUDA implementation notes
+ *           (2kiu.com/news/6063113)
+ *   [MAX]   "Why attention must compute the max first" -- naive, two-pass,
+ *           online and fused-online softmax (gsyq.cn/news/340375)
+ *   [LNXA]  "How to fuse cross-attention and layer-norm into a single CUDA
+ *           kernel?" (cms365.cn question page)
+ *
+ * What it computes is the plain definition, written out with no blocking,
+ * fusion or reordering:
+ *   s_j   = scale * <q_i, k_j>                    [MAX 5.2: divide QK^T by sqrt(d_k)]
+ *   mask  : an illegal position gets -inf before normalisation
+ *           (causal j > i, key padding j >= len_b, or an additive mask whose
+ *           -inf entries mark illegal keys)       [MMHA 1, 3.1, 4.2; MAX 2.4, 4.1]
+ *   p_j   = exp(s_j - max) / sum exp(s - max)    three separate passes, the
+ *                                                 naive softmax of [MAX 2.1]
+ *   o_i   = sum_j p_j v_j                        [MAX 4.1 fused_attn; LNXA
+ *                                                 knowledge points: S, P, O chain]
+ * Readings where the pages are silent or garbled (each is listed in the design
+ * notes of the repository):
+ *   - a row with no legal key produces o = 0 and raises FLAG_FULLY_MASKED_ROW
+ *     (the pages raise a global error flag on a bad softmax [LNXA knowledge
+ *     points, further thoughts]);
+ *   - the additive mask is added after scaling and is not itself scaled; only
+ *     an entry equal to -inf counts as a masked decision;
+ *   - padding lengths outside [0, Lk] raise FLAG_BAD_LENGTH and act clamped;
+ *   - pre-LayerNorm normalises each token over all H*D features with the
+ *     biased variance and eps inside the square root, then applies gamma and
+ *     beta; Q for head h is that token's slice [h*D, (h+1)*D)
+ *     [LNXA answer step 2]; the residual is added after attention
+ *     [LNXA answer step 4].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_CAUSAL = 1, OR_PADDING = 2, OR_ADDITIVE = 4 };
+enum { OR_FLAG_FULLY_MASKED_ROW = 1, OR_FLAG_NONFINITE = 2, OR_FLAG_BAD_LENGTH = 4 };
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* The mask decision for query i, key j of batch entry b.
+ * causal: future keys (j > i) are illegal [MMHA 4.2 kernel: row < col is masked].
+ * padding: keys at or beyond the sequence length are illegal [MMHA 3.1].
+ * additive: an entry of -inf marks an illegal key [MMHA 1: illegal logits are
+ * set to negative infinity before softmax normalisation]. */
+static int is_masked(unsigned kind, int64_t i, int64_t j, int64_t len_b, double add) {
+    if ((kind & OR_CAUSAL) && j > i) return 1;
+    if ((kind & OR_PADDING) && j >= len_b) return 1;
+    if ((kind & OR_ADDITIVE) && isinf(add) && add < 0) return 1;
+    return 0;
+}
+
+static uint32_t length_flags(unsigned kind, const int32_t* lens, int B, int Lk) {
+    uint32_t f = 0;
+    if (kind & OR_PADDING)
+        for (int b = 0; b < B; ++b)
+            if (lens[b] < 0 || lens[b] > Lk) f |= OR_FLAG_BAD_LENGTH;
+    return f;
+}
+
+/* One attention row: scores, mask, then the naive three-pass softmax of
+ * [MAX 2.1] (pass 1 the row max, pass 2 the sum of exp(s - max), pass 3 the
+ * normalised weights applied to V). s is caller scratch of length Lk; p, when
+ * not NULL, receives the softmax weights (0 for masked keys). */
+static uint32_t attention_row(const double* q, const double* K, const double* V,
+                              int Lk, int D, double scale, unsigned kind,
+                              int64_t i, int64_t len_b, const double* addrow,
+                              double* s, double* p, double* o) {
+    uint32_t flags = 0;
+    /* scores and mask decisions */
+    for (int j = 0; j < Lk; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += q[d] * K[(int64_t)j * D + d];
+        double add = (kind & OR_ADDITIVE) ? addrow[j] : 0.0;
+        if (is_masked(kind, i, j, len_b, add)) {
+            s[j] = -INFINITY;
+        } else {
+            s[j] = scale * dot;
+            if (kind & OR_ADDITIVE) s[j] += add;
+        }
+    }
+    /* pass 1: maximum over legal keys (a masked key holds -inf) */
+    double m = -INFINITY;
+    for (int j = 0; j < Lk; ++j)
+        if (!(s[j] <= m)) m = s[j]; /* a NaN score propagates */
+    if (m == -INFINITY) {
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (p) for (int j = 0; j < Lk; ++j) p[j] = 0.0;
+        return OR_FLAG_FULLY_MASKED_ROW;
+    }
+    /* pass 2: normaliser */
+    double z = 0.0;
+    for (int j = 0; j < Lk; ++j)
+        if (s[j] != -INFINITY) z += exp(s[j] - m);
+    /* pass 3: weights and the weighted sum of V over the legal keys */
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    for (int j = 0; j < Lk; ++j) {
+        if (s[j] == -INFINITY) {
+            if (p) p[j] = 0.0;
+            continue;
+        }
+        double w = exp(s[j] - m) / z;
+        if (p) p[j] = w;
+        for (int d = 0; d < D; ++d) o[d] += w * V[(int64_t)j * D + d];
+    }
+    for (int d = 0; d < D; ++d)
+        if (!isfinite(o[d])) flags |= OR_FLAG_NONFINITE;
+    return flags;
+}
+
+/* Full forward: q [B,H,Lq,D], k/v [B,H,Lk,D], out [B,H,Lq,D]; lens [B] (PADDING);
+ * add [B,1,Lq,Lk] (ADDITIVE, broadcast over heads). Returns the flag word. */
+uint32_t oracle_mha_fwd(const double* q, const double* k, const double* v,
+                        const int32_t* lens, const double* add, unsigned kind,
+                        int B, int H, int Lq, int Lk, int D, double scale, double* out) {
+    uint32_t flags = length_flags(kind, lens, B, Lk);
+    int64_t nrows = (int64_t)B * H * Lq;
+#pragma omp parallel reduction(| : flags)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t i = r % Lq, bh = r / Lq, b = bh / H;
+            const double* addrow = (kind & OR_ADDITIVE) ? add + ((int64_t)b * Lq + i) * Lk : NULL;
+            int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+            flags |= attention_row(q + r * D, k + bh * Lk * D, v + bh * Lk * D, Lk, D, scale,
+                                   kind, i, len_b, addrow, s, NULL, out + r * D);
+        }
+        free(s);
+    }
+    return flags;
+}
+
+/* Selected rows only: rows holds n triples (b, h, i); out receives n*D values. */
+uint32_t oracle_mha_rows(const double* q, const double* k, const double* v,
+                         const int32_t* lens, const double* add, unsigned kind,
+                         int B, int H, int Lq, int Lk, int D, double scale,
+                         const int64_t* rows, int64_t n, double* out) {
+    uint32_t flags = length_flags(kind, lens, B, Lk);
+#pragma omp parallel reduction(| : flags)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            int64_t bh = b * H + h;
+            const double* addrow = (kind & OR_ADDITIVE) ? add + (b * Lq + i) * Lk : NULL;
+            int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+            flags |= attention_row(q + (bh * Lq + i) * D, k + bh * Lk * D, v + bh * Lk * D, Lk,
+                                   D, scale, kind, i, len_b, addrow, s, NULL, out + r * D);
+        }
+        free(s);
+    }
+    return flags;
+}
+
+/* Softmax weights of one row (b, h, i): p receives Lk values. */
+uint32_t oracle_probs_row(const double* q, const double* k, const int32_t* lens,
+                          const double* add, unsigned kind, int B, int H, int Lq, int Lk,
+                          int D, double scale, int b, int h, int i, double* p) {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+    double* o = (double*)calloc((size_t)D, sizeof(double));
+    /* V = 0 keeps the row's weights the only output of interest */
+    double* vz = (double*)calloc((size_t)Lk * D + 1, sizeof(double));
+    int64_t bh = (int64_t)b * H + h;
+    const double* addrow = (kind & OR_ADDITIVE) ? add + ((int64_t)b * Lq + i) * Lk : NULL;
+    int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+    uint32_t f = attention_row(q + (bh * Lq + i) * D, k + bh * Lk * D, vz, Lk, D, scale, kind,
+                               i, len_b, addrow, s, p, o);
+    free(vz);
+    free(o);
+    free(s);
+    return f | length_flags(kind, lens, B, Lk);
+}
+
+/* Pre-LayerNorm of one token of F features [LNXA answer step 2]: mean, biased
+ * variance, (x - mean) / sqrt(var + eps), then gamma and beta. */
+static void layernorm_token(const double* x, const double* gamma, const double* beta,
+                            double eps, int F, double* y) {
+    double mean = 0.0;
+    for (int f = 0; f < F; ++f) mean += x[f];
+    mean /= F;
+    double var = 0.0;
+    for (int f = 0; f < F; ++f) var += (x[f] - mean) * (x[f] - mean);
+    var /= F;
+    double inv = 1.0 / sqrt(var + eps);
+    for (int f = 0; f < F; ++f) y[f] = (x[f] - mean) * inv * gamma[f] + beta[f];
+}
+
+void oracle_layernorm(const double* x, const double* gamma, const double* beta, double eps,
+                      int64_t ntok, int F, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t) layernorm_token(x + t * F, gamma, beta, eps, F, y + t * F);
+}
+
+/* Pre-LN cross-attention for selected rows: rows holds n triples (b, i, h);
+ * out receives n*D values out[b, i, h*D + d] = attention + residual.
+ * x, residual [B,Lq,H*D]; k, v [B,H,Lk,D]; gamma, beta [H*D]. residual may be NULL. */
+uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
+                             const int32_t* lens, const double* add, unsigned kind,
+                             const double* gamma, const double* beta, double eps,
+                             const double* residual, int B, int H, int Lq, int Lk, int D,
+                             double scale, const int64_t* rows, int64_t n, double* out) {
+    uint32_t flags = length_flags(kind, lens, B, Lk);
+    int F = H * D;
+#pragma omp parallel reduction(| : flags)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+        double* y = (double*)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
+            int64_t tok = b * Lq + i, bh = b * H + h;
+            layernorm_token(x + tok * F, gamma, beta, eps, F, y);
+            const double* addrow = (kind & OR_ADDITIVE) ? add + (b * Lq + i) * Lk : NULL;
+            int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+            double* o = out + r * D;
+            flags |= attention_row(y + h * D, k + bh * Lk * D, v + bh * Lk * D, Lk, D, scale,
+                                   kind, i, len_b, addrow, s, NULL, o);
+            if (residual)
+                for (int d = 0; d < D; ++d) o[d] += residual[tok * F + h * D + d];
+            for (int d = 0; d < D; ++d)
+                if (!isfinite(o[d])) flags |= OR_FLAG_NONFINITE;
+        }
+        free(y);
+        free(s);
+    }
+    return flags;
+}
+
+/* Full pre-LN cross-attention: out [B,Lq,H*D]. */
+uint32_t oracle_prenorm_cross_fwd(const double* x, const double* k, const double* v,
+                                  const int32_t* lens, const double* add, unsigned kind,
+                                  const double* gamma, const double* beta, double eps,
+                                  const double* residual, int B, int H, int Lq, int Lk, int D,
+                                  double scale, double* out) {
+    int64_t n = (int64_t)B * Lq * H;
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * 3 * (size_t)(n > 0 ? n : 1));
+    for (int64_t r = 0; r < n; ++r) {
+        rows[3 * r] = r / ((int64_t)Lq * H);
+        rows[3 * r + 1] = (r / H) % Lq;
+        rows[3 * r + 2] = r % H;
+    }
+    /* row r = ((b*Lq + i)*H + h) lands at out + r*D, i.e. out[b, i, h*D + d] */
+    uint32_t f = oracle_prenorm_rows(x, k, v, lens, add, kind, gamma, beta, eps, residual, B, H,
+                                     Lq, Lk, D, scale, rows, n, out);
+    free(rows);
+    return f;
+}
+
+/* Mask decisions as bytes: dec [B,Lq,Lk], 1 = masked. Heads share the mask. */
+void oracle_mask_decisions(const int32_t* lens, const double* add, unsigned kind, int B,
+                           int Lq, int Lk, uint8_t* dec) {
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = 0; i < Lq; ++i)
+            for (int64_t j = 0; j < Lk; ++j) {
+                int64_t idx = (b * Lq + i) * Lk + j;
+                double a = (kind & OR_ADDITIVE) ? add[idx] : 0.0;
+                int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+                dec[idx] = (uint8_t)is_masked(kind, i, j, len_b, a);
+            }
+}
+
+/* Number of legal (b, h, i, j) pairs: the work that counts as effective. */
+int64_t oracle_unmasked_pairs(const int32_t* lens, const double* add, unsigned kind, int B,
+                              int H, int Lq, int Lk) {
+    int64_t cnt = 0;
+#pragma omp parallel for reduction(+ : cnt) schedule(static)
+    for (int64_t bi = 0; bi < (int64_t)B * Lq; ++bi) {
+        int64_t b = bi / Lq, i = bi % Lq;
+        int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+        for (int64_t j = 0; j < Lk; ++j) {
+            double a = (kind & OR_ADDITIVE) ? add[bi * Lk + j] : 0.0;
+            if (!is_masked(kind, i, j, len_b, a)) cnt++;
+        }
+    }
+    return cnt * H;
+}
+
+/* Tiles of rm query rows by bn keys (aligned at multiples of rm and bn) that
+ * hold at least one legal pair ("computed") or none ("skipped"), summed over
+ * b and h: the whole-work skipping of [MMHA 2], decided by brute force over
+ * the mask decisions. counts[0] = computed, counts[1] = skipped. */
+void oracle_tile_counts(const int32_t* lens, const double* add, unsigned kind, int B, int H,
+                        int Lq, int Lk, int rm, int bn, int64_t* counts) {
+    int64_t comp = 0, skip = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+        for (int64_t i0 = 0; i0 < Lq; i0 += rm)
+            for (int64_t j0 = 0; j0 < Lk; j0 += bn) {
+                int legal = 0;
+                for (int64_t i = i0; i < i0 + rm && i < Lq && !legal; ++i)
+                    for (int64_t j = j0; j < j0 + bn && j < Lk; ++j) {
+                        double a = (kind & OR_ADDITIVE) ? add[(b * Lq + i) * Lk + j] : 0.0;
+                        if (!is_masked(kind, i, j, len_b, a)) { legal = 1; break; }
+                    }
+                if (legal) comp++; else skip++;
+            }
+    }
+    counts[0] = comp * H;
+    counts[1] = skip * H;
+}
+
+/* Rows with no legal key, summed over b and h. */
+int64_t oracle_fully_masked_rows(const int32_t* lens, const double* add, unsigned kind, int B,
+                                 int H, int Lq, int Lk) {
+    int64_t cnt = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+        for (int64_t i = 0; i < Lq; ++i) {
+            int legal = 0;
+            for (int64_t j = 0; j < Lk && !legal; ++j) {
+                double a = (kind & OR_ADDITIVE) ? add[(b * Lq + i) * Lk + j] : 0.0;
+                legal = !is_masked(kind, i, j, len_b, a);
+            }
+            if (!legal) cnt++;
+        }
+    }
+    return cnt * H;
+}
