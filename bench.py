@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark: fused masked multi-head attention forward on one MI355X.
+
+One step = one call of the library's hot path (one kernel launch) over one
+batch of seeded synthetic input already resident in HBM. W warm-up steps,
+then exactly K steps are timed between synchronisations with HIP events on
+the stream the kernel is launched on. The K timed steps are captured once as
+a HIP graph and replayed, so the figure is the GPU's throughput, not the
+host's launch rate; the eager (launch-per-call) time is reported beside it.
+
+Prints one JSON line: metric, value (effective TFLOP/s, masked-out work not
+counted), us_per_call, the roofline of the kernel and the fp64 CPU oracle's
+rate on the host cores (cpu_baseline). ``--config N`` picks workload N
+(default 2: fp32 B=4 H=8 L=128 D=64, causal + key padding).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "masked-MHA fwd effective TFLOP/s + µs/call; % of MFMA/HBM roofline (1 GPU)"
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}  # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+KERNEL_NAME = "mha_fwd_kernel"
+
+
+# ---------------------------------------------------------------------------
+# work accounting (plain counting from the mask definitions)
+# ---------------------------------------------------------------------------
+def legal_matrix(w: W.Workload, b: int) -> np.ndarray:
+    """bool [Lq, Lk]: legal (query, key) pairs of batch entry b (shared by heads)."""
+    i = np.arange(w.Lq)[:, None]
+    j = np.arange(w.Lk)[None, :]
+    ok = np.ones((w.Lq, w.Lk), bool)
+    if w.kind & W.CAUSAL:
+        ok &= j <= i
+    if w.kind & W.PADDING:
+        ok &= j < w.lens[b]
+    if w.kind & W.ADDITIVE:
+        ok &= ~np.isneginf(W.to_f64(w.add[b, 0], w.dtype))
+    return ok
+
+
+def work(w: W.Workload):
+    """(effective FLOPs, algorithmic bytes, legal pairs per (b, query row))."""
+    E = ESIZE[w.dtype]
+    pairs_row = np.stack([legal_matrix(w, b).sum(axis=1) for b in range(w.B)])  # [B, Lq]
+    flops = 4.0 * w.D * float(pairs_row.sum()) * w.H
+    keys_used = sum(int(legal_matrix(w, b).any(axis=0).sum()) for b in range(w.B))
+    kv = 2.0 * keys_used * w.H * w.D * E
+    if w.prenorm:
+        F = w.H * w.D
+        io = 2.0 * w.B * w.Lq * F * E + 2.0 * F * E  # x (also the residual) in, out; gamma, beta
+    else:
+        io = 2.0 * w.B * w.H * w.Lq * w.D * E  # Q in, O out
+    mask = 0.0
+    if w.kind & W.PADDING:
+        mask = 4.0 * w.B
+    elif w.kind & W.ADDITIVE:
+        mask = float(w.B * w.Lq * w.Lk * E)
+    return flops, io + kv + mask, pairs_row
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "masked_head_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        txt = f.read()
+    m = re.search(r"^kernel_sources_sha256_16:\s*(\S+)", txt, re.M)
+    t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+def gpu_setup(w: W.Workload):
+    import torch
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.int32:
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    d = {n: dev(getattr(w, n)) for n in ("q", "k", "v", "x", "gamma", "beta")}
+    d["mask"] = dev(w.lens) if w.kind & W.PADDING else (dev(w.add) if w.kind & W.ADDITIVE else None)
+    d["out"] = torch.empty_like(d["x"] if w.prenorm else d["q"])
+    return d
+
+
+def make_step(w: W.Workload, d):
+    import masked_head_attention_amd as M
+
+    if w.prenorm:
+        res = d["x"] if w.residual else None
+
+        def step():
+            M.prenorm_cross_fwd(d["x"], d["k"], d["v"], d["gamma"], d["beta"], w.eps,
+                                residual=res, mask=d["mask"], kind=w.kind, scale=w.scale,
+                                out=d["out"])
+    else:
+        def step():
+            M.fwd(d["q"], d["k"], d["v"], mask=d["mask"], kind=w.kind, scale=w.scale,
+                  out=d["out"])
+    return step
+
+
+def time_gpu(step, K: int, Wm: int, eager: bool):
+    """Seconds per step over exactly K steps (graph replay unless eager)."""
+    import torch
+
+    for _ in range(Wm):
+        step()
+    torch.cuda.synchronize()
+    g = None
+    if not eager:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(K):
+                step()
+        g.replay()  # one untimed replay of the captured steps
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if g is not None:
+        g.replay()
+    else:
+        for _ in range(K):
+            step()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / K
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+def cpu_baseline(w: W.Workload, pairs_row: np.ndarray, target_s: float):
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    all_rows = w.B * w.H * w.Lq
+
+    def rows_for(n):
+        idx = rng.choice(all_rows, size=min(n, all_rows), replace=False)
+        b, rem = idx // (w.H * w.Lq), idx % (w.H * w.Lq)
+        h, i = rem // w.Lq, rem % w.Lq
+        if w.prenorm:
+            return np.stack([b, i, h], 1), b, i
+        return np.stack([b, h, i], 1), b, i
+
+    add64 = w.f64("add")
+    args = {}
+    if w.prenorm:
+        x = w.f64("x")
+        args = dict(x=x, k=w.f64("k"), v=w.f64("v"), gamma=w.f64("gamma"), beta=w.f64("beta"),
+                    residual=x if w.residual else None)
+    else:
+        args = dict(q=w.f64("q"), k=w.f64("k"), v=w.f64("v"))
+
+    def run(rows):
+        if w.prenorm:
+            oracle.prenorm_rows(args["x"], args["k"], args["v"], args["gamma"], args["beta"],
+                                w.eps, rows, residual=args["residual"], kind=w.kind, lens=w.lens,
+                                add=add64, scale=w.scale, qfmt=w.dtype)
+        else:
+            oracle.mha_rows(args["q"], args["k"], args["v"], rows, w.kind, w.lens, add64,
+                            w.scale)
+
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    n0 = max(64, min(all_rows, 2048))
+    rows, b, i = rows_for(n0)
+    t0 = time.perf_counter()
+    run(rows)
+    t_cal = time.perf_counter() - t0
+    per_row = t_cal / len(rows)
+    n = int(min(all_rows, max(len(rows), target_s / max(per_row, 1e-9))))
+    reps = 1
+    if n >= all_rows and all_rows * per_row < target_s:
+        reps = max(1, int(target_s / max(all_rows * per_row, 1e-9)))
+    rows, b, i = rows_for(n)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run(rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * float(pairs_row[b, i].sum()) * reps
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {all_rows} (b,h,query) rows drawn at random (seed 1234)"
+                  f"{f', whole workload x{reps}' if reps > 1 else ''}; {dt:.1f} s of fp64 "
+                  "three-pass oracle work",
+        "seconds": dt,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(W.CONFIGS))
+    ap.add_argument("--eager", action="store_true",
+                    help="time launch-per-call steps instead of a graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run only a plain device copy of this size (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: every (batch, head) of this path is "
+              f"independent, so N={args.gpus} GPUs would each run the one-GPU kernel on a "
+              f"1/N share with no exchange; no multi-GPU figure is produced.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        return 0
+
+    import masked_head_attention_amd as M
+
+    w = W.config(args.config)
+    flops, alg_bytes, pairs_row = work(w)
+    d = gpu_setup(w)
+    M.init()
+    step = make_step(w, d)
+    M.get_flags(clear=True)
+    t_step = time_gpu(step, args.steps, args.warmup, args.eager)
+    t_eager = t_step if args.eager else time_gpu(step, min(args.steps, 100), 5, True)
+    flags = M.get_flags(clear=True)
+
+    ai = flops / alg_bytes
+    ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / t_step / 1e12,
+                "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg_bytes / t_step / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, pairs_row, args.cpu_seconds)
+
+    value = flops / t_step / 1e12
+    cfg = {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "D": w.D,
+           "mask": {0: "none", 1: "causal", 2: "padding", 3: "causal+padding", 4: "additive",
+                    5: "causal+additive"}[w.kind] + (" pre-LN cross-attention" if w.prenorm else ""),
+           "seed": w.seed, "effective_flops": flops, "algorithmic_bytes": alg_bytes,
+           "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"}
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_step * 1e3, "us_per_call": t_step * 1e6,
+        "eager_us_per_call": t_eager * 1e6, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded, workloads.py recipe)",
+        "config": cfg, "roofline": roof, "cpu_baseline": cpu, "device_flags": flags,
+        "kernel_sources_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

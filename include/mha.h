@@ -1,0 +1,141 @@
+/*
+ * mha.h -- C ABI of libmha: the fused masked multi-head attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MMHA]  "masked multi head attention" CUDA implementation notes
+ *           (2kiu.com/news/6063113)
+ *   [MAX]   "Why attention must compute the max first" (gsyq.cn/news/340375)
+ *   [LNXA]  "How to fuse cross-attention and layer-norm into a single CUDA
+ *           kernel?" (cms365.cn question page)
+ *
+ * One call is one kernel launch on the caller's stream. Inside it, for every
+ * (batch, head, query) row: S = scale * Q K^T, a causal / key-padding /
+ * additive mask applied before normalisation, a numerically stable online
+ * softmax (running row max, rescaled running sum), and P V accumulated in
+ * registers; the S/P tile never reaches device memory.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers to contiguous row-major memory owned by the
+ *     caller; libmha never frees or retains them. Every tensor pointer must be
+ *     16-byte aligned (4-byte for the int32 lengths).
+ *   - dtype selects float32, float16 or bfloat16 for every floating tensor of
+ *     the call (q, k, v, x, gamma, beta, residual, additive mask, out).
+ *     Accumulation is float32 in all cases; the output is rounded to nearest
+ *     even.
+ *   - stream is a hipStream_t (NULL = the null stream). Calls are
+ *     asynchronous: they return once the kernel is enqueued.
+ *   - Validation is synchronous and happens before any HIP call: on any
+ *     error status nothing is enqueued.
+ *   - Conditions found on the device are ORed into one 32-bit flag word per
+ *     device (MHA_FLAG_*), read with mha_get_flags.
+ *   - out must not alias an input. residual may alias x.
+ *   - Thread safety: calls from several host threads are safe; the flag word
+ *     and the debug-counter pointer are shared per process/device.
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MHA_F32 = 0, MHA_F16 = 1, MHA_BF16 = 2 } mha_dtype;
+
+/* Mask kinds (bit flags). [MMHA 1, 3.1]: an upper-triangular (causal) mask,
+ * a padding mask, or a custom mask; illegal logits become -inf before the
+ * softmax normalisation [MAX 2.4].
+ *   CAUSAL    key j is illegal for query i when j > i (top-left aligned, also
+ *             when Lq != Lk) [MMHA 4.2 kernel skeleton].
+ *   PADDING   mask points to int32 len[B] in device memory; keys j >= len[b]
+ *             are illegal for every query of batch entry b. A length outside
+ *             [0, Lk] acts clamped and raises MHA_FLAG_BAD_LENGTH.
+ *   ADDITIVE  mask points to a [B,1,Lq,Lk] tensor of dtype, shared by all
+ *             heads, added to the scaled logits; an entry equal to -inf marks
+ *             an illegal key (a large finite negative value is only a bias).
+ * PADDING and ADDITIVE are mutually exclusive (one mask pointer); CAUSAL
+ * combines with either. mask must be NULL unless PADDING or ADDITIVE is set. */
+enum { MHA_MASK_NONE = 0, MHA_MASK_CAUSAL = 1, MHA_MASK_PADDING = 2, MHA_MASK_ADDITIVE = 4 };
+
+typedef enum {
+    MHA_OK = 0,
+    MHA_E_NULL = 1,        /* a required pointer is NULL */
+    MHA_E_SHAPE = 2,       /* a negative dimension, or H*D beyond the supported width */
+    MHA_E_DTYPE = 3,       /* dtype is not one of mha_dtype */
+    MHA_E_MASK = 4,        /* unknown bits, PADDING with ADDITIVE, or mask NULL-ness wrong */
+    MHA_E_UNSUPPORTED = 5, /* D not in {16, 32, 64, 128} */
+    MHA_E_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned (lengths: 4-byte) */
+    MHA_E_OVERFLOW = 7,    /* an element count overflows int64 or the grid exceeds 2^31-1 */
+    MHA_E_NO_DEVICE = 8,   /* no usable HIP device / runtime error while preparing */
+    MHA_E_LAUNCH = 9,      /* the kernel launch itself failed */
+    MHA_E_ARG = 10         /* scale or eps not finite, scale < 0, eps < 0 */
+} mha_status;
+
+/* Device flag word bits (ORed by kernels, cleared by mha_get_flags). */
+enum {
+    MHA_FLAG_FULLY_MASKED_ROW = 1, /* a valid query row had no legal key: its output is 0
+                                      (pre-LN: the residual) [LNXA knowledge points: an
+                                      error flag is raised when the softmax goes bad] */
+    MHA_FLAG_NONFINITE = 2,        /* a stored output value is NaN or infinite */
+    MHA_FLAG_BAD_LENGTH = 4        /* a padding length lies outside [0, Lk] */
+};
+
+/* Allocate (once) and zero the current device's flag word. Optional: the
+ * first call on a device does it otherwise; call it before capturing launches
+ * into a HIP graph so that no allocation happens during capture. */
+mha_status mha_init(void);
+
+/* Masked multi-head self/cross attention forward [MMHA 2, 4.2; MAX 2.4].
+ *   q    [B,H,Lq,D]   queries
+ *   k, v [B,H,Lk,D]   keys and values
+ *   mask see the mask kinds above
+ *   out  [B,H,Lq,D]   o[b,h,i,:] = sum_j softmax_j(scale*q.k_j (+ mask)) v_j over
+ *                     the legal keys j; 0 for a row with no legal key.
+ *   scale >= 0, finite (1/sqrt(D) is the usual choice [MAX 5.2]).
+ * B, H or Lq equal to 0 is an empty call (MHA_OK, nothing enqueued). Lk may
+ * be 0: every row is then fully masked. Other sizes must be >= 0;
+ * D must be 16, 32, 64 or 128. */
+mha_status mha_fwd(const void* q, const void* k, const void* v, const void* mask,
+                   unsigned mask_kind, int B, int H, int Lq, int Lk, int D, float scale,
+                   mha_dtype dtype, void* stream, void* out);
+
+/* Pre-LayerNorm cross-attention with the residual added in the epilogue
+ * [LNXA answer steps 1-4]: for token (b,i) the features x[b,i,:] (H*D of
+ * them) are normalised with their mean and biased variance,
+ * y = (x - mean) / sqrt(var + eps) * gamma + beta, and Q for head h is
+ * y[h*D:(h+1)*D]; then attention over k, v as in mha_fwd, and
+ *   out[b,i,h*D+d] = attention + residual[b,i,h*D+d]   (residual may be NULL).
+ *   x, residual, out [B,Lq,H*D];  gamma, beta [H*D];  k, v [B,H,Lk,D].
+ *   eps >= 0 and finite. H*D must not exceed 65536.
+ * A fully masked row stores the residual (or 0). */
+mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, const void* mask,
+                                 unsigned mask_kind, const void* gamma, const void* beta,
+                                 float eps, const void* residual, int B, int H, int Lq, int Lk,
+                                 int D, float scale, mha_dtype dtype, void* stream, void* out);
+
+/* Synchronise stream, then copy the current device's flag word to *flags;
+ * clear != 0 resets it to 0 afterwards. The word is per device, not per
+ * stream: launches on other streams that have not finished are not seen. */
+mha_status mha_get_flags(void* stream, uint32_t* flags, int clear);
+
+/* Debug counters [MAX 6: count executions with device atomics]: a device
+ * pointer to 3 uint64 values, or NULL to stop counting. While set, every
+ * launch adds (tiles computed, tiles skipped, valid rows with no legal key).
+ * A tile is mha_tile_config's rows x keys block, aligned at multiples of its
+ * size; it is skipped when every pair in it is masked [MMHA 2]. The pointer
+ * is process-wide; the caller owns and zeroes the memory. */
+mha_status mha_set_debug_counters(uint64_t* dev_counters);
+
+/* Tile of the skip decision for a dtype and D: *rows query rows by *keys keys. */
+mha_status mha_tile_config(mha_dtype dtype, int D, unsigned mask_kind, int* rows, int* keys);
+
+/* Human-readable name of a status code (static string). */
+const char* mha_status_str(mha_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

@@ -1,0 +1,143 @@
+"""masked_head_attention_amd: fused masked multi-head attention forward for
+AMD Instinct MI355X (gfx950).
+
+Thin binding over libmha's C ABI (include/mha.h): it checks each tensor's
+device, dtype, shape and contiguity, allocates the output if asked, and passes
+raw device pointers plus the current HIP stream. Every step of the attention
+runs in the HIP kernels of libmha; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+from ._abi import (ADDITIVE, BF16, CAUSAL, F16, F32, FLAG_BAD_LENGTH, FLAG_FULLY_MASKED_ROW,
+                   FLAG_NONFINITE, MASK_NONE, PADDING, MhaError, check, lib)
+
+__all__ = ["fwd", "prenorm_cross_fwd", "get_flags", "set_debug_counters", "tile_config",
+           "init", "MhaError", "CAUSAL", "PADDING", "ADDITIVE", "MASK_NONE",
+           "FLAG_FULLY_MASKED_ROW", "FLAG_NONFINITE", "FLAG_BAD_LENGTH"]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mask_arg(mask, kind, B, Lq, Lk, dtype):
+    torch = _torch()
+    if kind & PADDING:
+        return _dev(mask, "mask (lengths)", torch.int32, (B,))
+    if kind & ADDITIVE:
+        return _dev(mask, "mask (additive)", dtype, (B, 1, Lq, Lk))
+    if mask is not None:
+        raise ValueError("mask given but mask kind has neither PADDING nor ADDITIVE")
+    return None
+
+
+def init() -> None:
+    """Allocate the current device's flag word (optional; see mha_init)."""
+    check(lib().mha_init(), "mha_init")
+
+
+def fwd(q, k, v, mask=None, kind: int = MASK_NONE, scale: Optional[float] = None, out=None,
+        stream=None):
+    """Masked MHA forward. q [B,H,Lq,D], k/v [B,H,Lk,D] -> out [B,H,Lq,D]."""
+    torch = _torch()
+    _dev(q, "q")
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    _dev(k, "k", q.dtype, (B, H, Lk, D))
+    _dev(v, "v", q.dtype, (B, H, Lk, D))
+    m = _mask_arg(mask, kind, B, Lq, Lk, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, (B, H, Lq, D))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().mha_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(m), kind, B, H, Lq, Lk, D, scale,
+                       _dtype_code(q), _stream(stream), _ptr(out))
+    check(st, "mha_fwd")
+    return out
+
+
+def prenorm_cross_fwd(x, k, v, gamma, beta, eps: float = 1e-5, residual=None, mask=None,
+                      kind: int = MASK_NONE, scale: Optional[float] = None, out=None, stream=None):
+    """Pre-LN cross-attention + residual. x [B,Lq,H*D], k/v [B,H,Lk,D] -> out [B,Lq,H*D]."""
+    torch = _torch()
+    _dev(x, "x")
+    B, Lq, F = x.shape
+    _, H, Lk, D = k.shape
+    if H * D != F:
+        raise ValueError("x feature width must equal H*D")
+    _dev(k, "k", x.dtype, (B, H, Lk, D))
+    _dev(v, "v", x.dtype, (B, H, Lk, D))
+    _dev(gamma, "gamma", x.dtype, (F,))
+    _dev(beta, "beta", x.dtype, (F,))
+    _dev(residual, "residual", x.dtype, (B, Lq, F))
+    m = _mask_arg(mask, kind, B, Lq, Lk, x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype, (B, Lq, F))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().mha_prenorm_cross_fwd(_ptr(x), _ptr(k), _ptr(v), _ptr(m), kind, _ptr(gamma),
+                                     _ptr(beta), float(eps), _ptr(residual), B, H, Lq, Lk, D,
+                                     scale, _dtype_code(x), _stream(stream), _ptr(out))
+    check(st, "mha_prenorm_cross_fwd")
+    return out
+
+
+def get_flags(clear: bool = True, stream=None) -> int:
+    """Synchronise the stream and read (and by default clear) the device flag word."""
+    f = ctypes.c_uint32(0)
+    check(lib().mha_get_flags(_stream(stream), ctypes.byref(f), int(clear)), "mha_get_flags")
+    return int(f.value)
+
+
+def set_debug_counters(counters) -> None:
+    """Point the kernels at an int64 GPU tensor of 3 counters, or None to stop."""
+    torch = _torch()
+    if counters is not None:
+        _dev(counters, "counters", torch.int64, (3,))
+    check(lib().mha_set_debug_counters(_ptr(counters)), "mha_set_debug_counters")
+
+
+def tile_config(dtype_code: int, D: int, kind: int = MASK_NONE):
+    """(rows, keys) of the tile the skip decision is made on."""
+    r, k = ctypes.c_int(0), ctypes.c_int(0)
+    check(lib().mha_tile_config(dtype_code, D, kind, ctypes.byref(r), ctypes.byref(k)),
+          "mha_tile_config")
+    return r.value, k.value

@@ -1,0 +1,60 @@
+"""Build libmha.so in-tree with hipcc for gfx950.
+
+Every translation unit is compiled for gfx950 only, at -O3, with packed fp32
+instructions disabled (the compiler then emits scalar v_fma_f32/v_mul_f32 for
+float pairs). The per-dtype kernel units compile in parallel.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libmha.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+SOURCES = ["mha_api.hip", "mha_inst_f32.hip", "mha_inst_f16.hip", "mha_inst_bf16.hip"]
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+         "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
+         f"-I{CSRC}"]
+
+
+def _compile(src: str, obj: str, extra, verbose: bool) -> None:
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    if err.strip() and verbose:
+        print(err, flush=True)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        futs = [ex.submit(_compile, s, o, list(extra), verbose) for s, o in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    import sys
+
+    print(build(verbose=True, extra=sys.argv[1:]))

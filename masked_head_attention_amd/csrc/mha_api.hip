@@ -1,0 +1,231 @@
+// mha_api.hip -- the C ABI of libmha: argument validation, the per-device
+// flag word, dispatch to a kernel instantiation, launch on the caller's stream.
+//
+// Validation is synchronous and completes before the first HIP call, so an
+// invalid call enqueues nothing -- the launch-configuration check of
+// [MMHA 4.3] ("masked multi head attention" CUDA notes, 2kiu.com/news/6063113),
+// made a status code instead of a printf.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "mha.h"
+#include "mha_launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+uint32_t* g_flags[kMaxDevices] = {};
+std::atomic<unsigned long long*> g_counters{nullptr};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+bool count_ok(std::initializer_list<int64_t> dims, int64_t esize) {
+  int64_t r = esize;
+  for (int64_t d : dims)
+    if (!mul_ok(r, d, &r)) return false;
+  return true;
+}
+
+int elem_size(mha_dtype t) { return t == MHA_F32 ? 4 : 2; }
+
+// The current device's flag word, allocated (and zeroed) on first use.
+mha_status device_flags(uint32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MHA_E_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_flags[dev]) {
+    void* p = nullptr;
+    if (hipMalloc(&p, 256) != hipSuccess) return MHA_E_NO_DEVICE;
+    if (hipMemset(p, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(p);
+      return MHA_E_NO_DEVICE;
+    }
+    g_flags[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_flags[dev];
+  return MHA_OK;
+}
+
+struct Call {
+  const void* q;
+  const void* x;
+  const void* k;
+  const void* v;
+  const void* mask;
+  unsigned kind;
+  const void* gamma;
+  const void* beta;
+  float eps;
+  const void* residual;
+  int B, H, Lq, Lk, D;
+  float scale;
+  mha_dtype dtype;
+  void* stream;
+  void* out;
+  bool prenorm;
+};
+
+mha_status validate(const Call& c) {
+  if (c.dtype != MHA_F32 && c.dtype != MHA_F16 && c.dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (c.kind & ~7u) return MHA_E_MASK;
+  if ((c.kind & MHA_MASK_PADDING) && (c.kind & MHA_MASK_ADDITIVE)) return MHA_E_MASK;
+  const bool wants_mask = (c.kind & (MHA_MASK_PADDING | MHA_MASK_ADDITIVE)) != 0;
+  if (!wants_mask && c.mask) return MHA_E_MASK;
+  if (c.B < 0 || c.H < 0 || c.Lq < 0 || c.Lk < 0) return MHA_E_SHAPE;
+  if (c.D != 16 && c.D != 32 && c.D != 64 && c.D != 128) return MHA_E_UNSUPPORTED;
+  if (!std::isfinite(c.scale) || c.scale < 0.f) return MHA_E_ARG;
+  if (c.prenorm) {
+    if (!std::isfinite(c.eps) || c.eps < 0.f) return MHA_E_ARG;
+    if ((int64_t)c.H * c.D > 65536) return MHA_E_SHAPE;
+  }
+  if (c.B == 0 || c.H == 0 || c.Lq == 0) return MHA_OK;  // empty call
+  if (wants_mask && !c.mask) return MHA_E_NULL;
+  if (!c.out || (c.prenorm ? !c.x : !c.q)) return MHA_E_NULL;
+  if (c.Lk > 0 && (!c.k || !c.v)) return MHA_E_NULL;
+  if (c.prenorm && (!c.gamma || !c.beta)) return MHA_E_NULL;
+  const void* ptrs16[] = {c.q, c.x, c.k, c.v, c.out, c.gamma, c.beta, c.residual,
+                          (c.kind & MHA_MASK_ADDITIVE) ? c.mask : nullptr};
+  for (const void* p : ptrs16)
+    if (p && !aligned(p, 16)) return MHA_E_ALIGN;
+  if ((c.kind & MHA_MASK_PADDING) && !aligned(c.mask, 4)) return MHA_E_ALIGN;
+  const int64_t E = elem_size(c.dtype);
+  if (!count_ok({c.B, c.H, c.Lq, c.D}, E) || !count_ok({c.B, c.H, c.Lk, c.D}, E) ||
+      !count_ok({c.B, c.Lq, c.Lk}, E))
+    return MHA_E_OVERFLOW;
+  int bm = 0, tr = 0, tk = 0;
+  if (c.dtype == MHA_F32) mha::tile_shape_f32(c.D, &bm, &tr, &tk);
+  else if (c.dtype == MHA_F16) mha::tile_shape_f16(c.D, &bm, &tr, &tk);
+  else mha::tile_shape_bf16(c.D, &bm, &tr, &tk);
+  const int64_t grid = (int64_t)c.B * c.H * ((c.Lq + bm - 1) / bm);
+  if (grid > 0x7fffffffLL) return MHA_E_OVERFLOW;
+  return MHA_OK;
+}
+
+mha_status run(const Call& c) {
+  mha_status st = validate(c);
+  if (st != MHA_OK) return st;
+  if (c.B == 0 || c.H == 0 || c.Lq == 0) return MHA_OK;
+  uint32_t* flags = nullptr;
+  st = device_flags(&flags);
+  if (st != MHA_OK) return st;
+  mha::Params p{};
+  p.q = c.q;
+  p.k = c.k;
+  p.v = c.v;
+  p.lens = (c.kind & MHA_MASK_PADDING) ? static_cast<const int32_t*>(c.mask) : nullptr;
+  p.add = (c.kind & MHA_MASK_ADDITIVE) ? c.mask : nullptr;
+  p.x = c.x;
+  p.gamma = c.gamma;
+  p.beta = c.beta;
+  p.residual = c.residual;
+  p.out = c.out;
+  p.B = c.B;
+  p.H = c.H;
+  p.Lq = c.Lq;
+  p.Lk = c.Lk;
+  p.kind = c.kind & (MHA_MASK_CAUSAL | MHA_MASK_PADDING);
+  p.c = (float)((double)c.scale * 1.4426950408889634);  // log2(e): exp(x) = 2^(x log2 e)
+  p.eps = c.eps;
+  p.add_vec = ((int64_t)c.Lk * elem_size(c.dtype)) % 16 == 0;
+  p.flags = flags;
+  p.counters = g_counters.load(std::memory_order_acquire);
+  const bool add = (c.kind & MHA_MASK_ADDITIVE) != 0;
+  hipStream_t s = static_cast<hipStream_t>(c.stream);
+  hipError_t e;
+  if (c.dtype == MHA_F32) e = mha::launch_f32(p, c.D, add, c.prenorm, s);
+  else if (c.dtype == MHA_F16) e = mha::launch_f16(p, c.D, add, c.prenorm, s);
+  else e = mha::launch_bf16(p, c.D, add, c.prenorm, s);
+  return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status mha_init(void) {
+  uint32_t* f = nullptr;
+  return device_flags(&f);
+}
+
+mha_status mha_fwd(const void* q, const void* k, const void* v, const void* mask,
+                   unsigned mask_kind, int B, int H, int Lq, int Lk, int D, float scale,
+                   mha_dtype dtype, void* stream, void* out) {
+  Call c{q, nullptr, k, v, mask, mask_kind, nullptr, nullptr, 0.f, nullptr,
+         B, H, Lq, Lk, D, scale, dtype, stream, out, false};
+  return run(c);
+}
+
+mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, const void* mask,
+                                 unsigned mask_kind, const void* gamma, const void* beta,
+                                 float eps, const void* residual, int B, int H, int Lq, int Lk,
+                                 int D, float scale, mha_dtype dtype, void* stream, void* out) {
+  Call c{nullptr, x, k, v, mask, mask_kind, gamma, beta, eps, residual,
+         B, H, Lq, Lk, D, scale, dtype, stream, out, true};
+  return run(c);
+}
+
+mha_status mha_get_flags(void* stream, uint32_t* flags, int clear) {
+  if (!flags) return MHA_E_NULL;
+  uint32_t* dflags = nullptr;
+  mha_status st = device_flags(&dflags);
+  if (st != MHA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MHA_E_NO_DEVICE;
+  if (hipMemcpy(flags, dflags, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return MHA_E_NO_DEVICE;
+  if (clear) {
+    if (hipMemsetAsync(dflags, 0, sizeof(uint32_t), s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return MHA_E_NO_DEVICE;
+  }
+  return MHA_OK;
+}
+
+mha_status mha_set_debug_counters(uint64_t* dev_counters) {
+  if (dev_counters && !aligned(dev_counters, 8)) return MHA_E_ALIGN;
+  g_counters.store(reinterpret_cast<unsigned long long*>(dev_counters), std::memory_order_release);
+  return MHA_OK;
+}
+
+mha_status mha_tile_config(mha_dtype dtype, int D, unsigned mask_kind, int* rows, int* keys) {
+  if (!rows || !keys) return MHA_E_NULL;
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (mask_kind & ~7u) return MHA_E_MASK;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
+  int bm = 0;
+  if (dtype == MHA_F32) mha::tile_shape_f32(D, &bm, rows, keys);
+  else if (dtype == MHA_F16) mha::tile_shape_f16(D, &bm, rows, keys);
+  else mha::tile_shape_bf16(D, &bm, rows, keys);
+  return MHA_OK;
+}
+
+const char* mha_status_str(mha_status s) {
+  switch (s) {
+    case MHA_OK: return "MHA_OK";
+    case MHA_E_NULL: return "MHA_E_NULL: a required pointer is NULL";
+    case MHA_E_SHAPE: return "MHA_E_SHAPE: invalid dimension";
+    case MHA_E_DTYPE: return "MHA_E_DTYPE: unknown dtype";
+    case MHA_E_MASK: return "MHA_E_MASK: invalid mask kind or mask pointer";
+    case MHA_E_UNSUPPORTED: return "MHA_E_UNSUPPORTED: D must be 16, 32, 64 or 128";
+    case MHA_E_ALIGN: return "MHA_E_ALIGN: a tensor pointer is misaligned";
+    case MHA_E_OVERFLOW: return "MHA_E_OVERFLOW: sizes overflow";
+    case MHA_E_NO_DEVICE: return "MHA_E_NO_DEVICE: no usable HIP device";
+    case MHA_E_LAUNCH: return "MHA_E_LAUNCH: kernel launch failed";
+    case MHA_E_ARG: return "MHA_E_ARG: scale or eps out of range";
+  }
+  return "unknown mha_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// mha_launch.hpp -- host-side launch of one kernel instantiation per
+// (dtype, D, additive, pre-LN). Included by one translation unit per dtype.
+#pragma once
+
+#include "mha_kernel.hpp"
+
+namespace mha {
+
+// Query rows per workgroup and keys per wave tile for (T, D).
+template <typename T, int D>
+constexpr int block_rows() { return 32 * TileCfg<T, D>::NQ; }
+
+template <typename T, int D, bool ADD, bool PRE>
+hipError_t launch_one(Params p, hipStream_t stream) {
+  using Cfg = TileCfg<T, D>;
+  p.nqblk = (p.Lq + block_rows<T, D>() - 1) / block_rows<T, D>();
+  const long long grid = (long long)p.B * p.H * p.nqblk;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mha_fwd_kernel<T, D, ADD, PRE>), dim3((unsigned)grid),
+                     dim3(64 * Cfg::NQ * Cfg::NK), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const Params& p, bool add, bool pre, hipStream_t s) {
+  if (add) return pre ? launch_one<T, D, true, true>(p, s) : launch_one<T, D, true, false>(p, s);
+  return pre ? launch_one<T, D, false, true>(p, s) : launch_one<T, D, false, false>(p, s);
+}
+
+template <typename T>
+hipError_t launch_dtype(const Params& p, int D, bool add, bool pre, hipStream_t s) {
+  switch (D) {
+    case 16: return launch_d<T, 16>(p, add, pre, s);
+    case 32: return launch_d<T, 32>(p, add, pre, s);
+    case 64: return launch_d<T, 64>(p, add, pre, s);
+    case 128: return launch_d<T, 128>(p, add, pre, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+void tile_shape(int D, int* rows_per_block, int* tile_rows, int* tile_keys) {
+  switch (D) {
+#define MHA_TILE_CASE(DD)                                     \
+  case DD:                                                    \
+    *rows_per_block = block_rows<T, DD>();                    \
+    *tile_rows = 32;                                          \
+    *tile_keys = TileCfg<T, DD>::BN;                          \
+    return;
+    MHA_TILE_CASE(16)
+    MHA_TILE_CASE(32)
+    MHA_TILE_CASE(64)
+    MHA_TILE_CASE(128)
+#undef MHA_TILE_CASE
+    default: *rows_per_block = *tile_rows = *tile_keys = 0;
+  }
+}
+
+// Entry points defined per dtype.
+hipError_t launch_f32(const Params& p, int D, bool add, bool pre, hipStream_t s);
+hipError_t launch_f16(const Params& p, int D, bool add, bool pre, hipStream_t s);
+hipError_t launch_bf16(const Params& p, int D, bool add, bool pre, hipStream_t s);
+void tile_shape_f32(int D, int* bm, int* rows, int* keys);
+void tile_shape_f16(int D, int* bm, int* rows, int* keys);
+void tile_shape_bf16(int D, int* bm, int* rows, int* keys);
+
+}  // namespace mha

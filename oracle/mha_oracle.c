@@ -35,7 +35,9 @@
  *   - pre-LayerNorm normalises each token over all H*D features with the
  *     biased variance and eps inside the square root, then applies gamma and
  *     beta; Q for head h is that token's slice [h*D, (h+1)*D)
- *     [LNXA answer step 2]; the residual is added after attention
+ *     [LNXA answer step 2], held in the call's working precision (rounded
+ *     to float16/bfloat16/float32, the FP16/BF16 mixed precision of the LNXA
+ *     knowledge points); the residual is added after attention
  *     [LNXA answer step 4].
  */
 #include <math.h>
@@ -83,6 +85,31 @@ static uint32_t length_flags(unsigned kind, const int32_t* lens, int B, int Lk) 
         for (int b = 0; b < B; ++b)
             if (lens[b] < 0 || lens[b] > Lk) f |= OR_FLAG_BAD_LENGTH;
     return f;
+}
+
+/* Round x to nearest (ties to even) in a binary floating format with p
+ * significand bits, smallest normal exponent emin and largest finite value
+ * maxv: the plain definition (spacing 2^(e - p + 1) at the leading exponent
+ * e, clamped at emin for subnormals; beyond maxv after rounding -> inf).
+ * fmt: 0 none, 1 float32, 2 float16, 3 bfloat16. */
+double oracle_round(double x, int fmt) {
+    int p, emin;
+    double maxv;
+    switch (fmt) {
+        case 1: p = 24; emin = -126; maxv = 3.4028234663852886e38; break;
+        case 2: p = 11; emin = -14; maxv = 65504.0; break;
+        case 3: p = 8; emin = -126; maxv = 3.3895313892515355e38; break;
+        default: return x;
+    }
+    if (!isfinite(x) || x == 0.0) return x;
+    int e;
+    frexp(x, &e); /* |x| in [2^(e-1), 2^e) */
+    int lead = e - 1;
+    if (lead < emin) lead = emin;
+    double spacing = ldexp(1.0, lead - (p - 1));
+    double r = nearbyint(x / spacing) * spacing; /* default mode: nearest, ties to even */
+    if (fabs(r) > maxv) r = copysign(INFINITY, x);
+    return r;
 }
 
 /* One attention row: scores, mask, then the naive three-pass softmax of
@@ -203,7 +230,7 @@ uint32_t oracle_probs_row(const double* q, const double* k, const int32_t* lens,
 /* Pre-LayerNorm of one token of F features [LNXA answer step 2]: mean, biased
  * variance, (x - mean) / sqrt(var + eps), then gamma and beta. */
 static void layernorm_token(const double* x, const double* gamma, const double* beta,
-                            double eps, int F, double* y) {
+                            double eps, int F, int qfmt, double* y) {
     double mean = 0.0;
     for (int f = 0; f < F; ++f) mean += x[f];
     mean /= F;
@@ -211,21 +238,26 @@ static void layernorm_token(const double* x, const double* gamma, const double* 
     for (int f = 0; f < F; ++f) var += (x[f] - mean) * (x[f] - mean);
     var /= F;
     double inv = 1.0 / sqrt(var + eps);
-    for (int f = 0; f < F; ++f) y[f] = (x[f] - mean) * inv * gamma[f] + beta[f];
+    for (int f = 0; f < F; ++f) y[f] = oracle_round((x[f] - mean) * inv * gamma[f] + beta[f], qfmt);
 }
 
 void oracle_layernorm(const double* x, const double* gamma, const double* beta, double eps,
-                      int64_t ntok, int F, double* y) {
+                      int64_t ntok, int F, int qfmt, double* y) {
 #pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < ntok; ++t) layernorm_token(x + t * F, gamma, beta, eps, F, y + t * F);
+    for (int64_t t = 0; t < ntok; ++t)
+        layernorm_token(x + t * F, gamma, beta, eps, F, qfmt, y + t * F);
 }
 
 /* Pre-LN cross-attention for selected rows: rows holds n triples (b, i, h);
  * out receives n*D values out[b, i, h*D + d] = attention + residual.
- * x, residual [B,Lq,H*D]; k, v [B,H,Lk,D]; gamma, beta [H*D]. residual may be NULL. */
+ * x, residual [B,Lq,H*D]; k, v [B,H,Lk,D]; gamma, beta [H*D]. residual may be NULL.
+ * qfmt: the normalised query is held in the working precision of the call
+ * (FP16/BF16 mixed precision, gamma and beta applied straight onto the Q
+ * matrix with half-precision FMAs [LNXA knowledge points; answer step 2]),
+ * so it is rounded to that format (oracle_round) before the attention. */
 uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
                              const int32_t* lens, const double* add, unsigned kind,
-                             const double* gamma, const double* beta, double eps,
+                             const double* gamma, const double* beta, double eps, int qfmt,
                              const double* residual, int B, int H, int Lq, int Lk, int D,
                              double scale, const int64_t* rows, int64_t n, double* out) {
     uint32_t flags = length_flags(kind, lens, B, Lk);
@@ -238,7 +270,7 @@ uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
         for (int64_t r = 0; r < n; ++r) {
             int64_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
             int64_t tok = b * Lq + i, bh = b * H + h;
-            layernorm_token(x + tok * F, gamma, beta, eps, F, y);
+            layernorm_token(x + tok * F, gamma, beta, eps, F, qfmt, y);
             const double* addrow = (kind & OR_ADDITIVE) ? add + (b * Lq + i) * Lk : NULL;
             int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
             double* o = out + r * D;
@@ -258,7 +290,7 @@ uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
 /* Full pre-LN cross-attention: out [B,Lq,H*D]. */
 uint32_t oracle_prenorm_cross_fwd(const double* x, const double* k, const double* v,
                                   const int32_t* lens, const double* add, unsigned kind,
-                                  const double* gamma, const double* beta, double eps,
+                                  const double* gamma, const double* beta, double eps, int qfmt,
                                   const double* residual, int B, int H, int Lq, int Lk, int D,
                                   double scale, double* out) {
     int64_t n = (int64_t)B * Lq * H;
@@ -269,8 +301,8 @@ uint32_t oracle_prenorm_cross_fwd(const double* x, const double* k, const double
         rows[3 * r + 2] = r % H;
     }
     /* row r = ((b*Lq + i)*H + h) lands at out + r*D, i.e. out[b, i, h*D + d] */
-    uint32_t f = oracle_prenorm_rows(x, k, v, lens, add, kind, gamma, beta, eps, residual, B, H,
-                                     Lq, Lk, D, scale, rows, n, out);
+    uint32_t f = oracle_prenorm_rows(x, k, v, lens, add, kind, gamma, beta, eps, qfmt, residual,
+                                     B, H, Lq, Lk, D, scale, rows, n, out);
     free(rows);
     return f;
 }
