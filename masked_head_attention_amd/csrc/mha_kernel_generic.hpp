@@ -1,4 +1,5 @@
-// mha_kernel.hpp -- fused masked multi-head attention forward for gfx950 (CDNA4).
+// mha_kernel_generic.hpp -- fused masked multi-head attention forward for gfx950
+// (CDNA4), register-staged variant (used for float32).
 //
 // Sources (web pages, cited by title and section):
 //   [MMHA]  "masked multi head attention" CUDA implementation notes (2kiu.com/news/6063113)
@@ -39,172 +40,9 @@
 //     registers; the epilogue adds the residual [LNXA answer steps 2, 4].
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
+#include "mha_common.hpp"
 
 namespace mha {
-
-enum : unsigned { K_CAUSAL = 1u, K_PADDING = 2u, K_ADDITIVE = 4u };
-enum : uint32_t { F_FULLY_MASKED_ROW = 1u, F_NONFINITE = 2u, F_BAD_LENGTH = 4u };
-
-struct Params {
-  const void* q;         // [B,H,Lq,D]
-  const void* k;         // [B,H,Lk,D]
-  const void* v;         // [B,H,Lk,D]
-  const int32_t* lens;   // [B] (PADDING)
-  const void* add;       // [B,1,Lq,Lk] (ADDITIVE)
-  const void* x;         // [B,Lq,H*D] (pre-LN)
-  const void* gamma;     // [H*D]
-  const void* beta;      // [H*D]
-  const void* residual;  // [B,Lq,H*D] or null
-  void* out;             // [B,H,Lq,D] or [B,Lq,H*D] (pre-LN)
-  int B, H, Lq, Lk;
-  int nqblk;             // query blocks per (b, h)
-  unsigned kind;         // K_CAUSAL | K_PADDING (ADDITIVE is a template switch)
-  float c;               // scale * log2(e)
-  float eps;
-  int add_vec;           // additive-mask rows are 16-byte aligned
-  uint32_t* flags;
-  unsigned long long* counters;  // [3] or null
-};
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Eight consecutive elements of type T, as raw 16-byte words.
-template <typename T>
-struct Frag8 {
-  static constexpr int W = sizeof(T) / 2;  // uint4 words: 1 for half types, 2 for float
-  uint4 u[W];
-};
-
-// ---- element conversions -------------------------------------------------
-__device__ inline float lo_f(uint32_t w, _Float16*) {
-  return (float)__builtin_bit_cast(f16x2, w)[0];
-}
-__device__ inline float hi_f(uint32_t w, _Float16*) {
-  return (float)__builtin_bit_cast(f16x2, w)[1];
-}
-__device__ inline float lo_f(uint32_t w, __bf16*) { return __uint_as_float(w << 16); }
-__device__ inline float hi_f(uint32_t w, __bf16*) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ inline uint32_t pack2(float a, float b, _Float16*) {
-  f16x2 h = {(_Float16)a, (_Float16)b};  // v_cvt_pk_f16_f32, round to nearest even
-  return __builtin_bit_cast(uint32_t, h);
-}
-__device__ inline uint32_t pack2(float a, float b, __bf16*) {
-  bf16x2 h = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32, round to nearest even
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-template <typename T>
-__device__ inline void unpack8(const Frag8<T>& f, float (&x)[8]) {
-  if constexpr (sizeof(T) == 4) {
-    x[0] = __uint_as_float(f.u[0].x); x[1] = __uint_as_float(f.u[0].y);
-    x[2] = __uint_as_float(f.u[0].z); x[3] = __uint_as_float(f.u[0].w);
-    x[4] = __uint_as_float(f.u[1].x); x[5] = __uint_as_float(f.u[1].y);
-    x[6] = __uint_as_float(f.u[1].z); x[7] = __uint_as_float(f.u[1].w);
-  } else {
-    T* tag = nullptr;
-    const uint32_t w[4] = {f.u[0].x, f.u[0].y, f.u[0].z, f.u[0].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = lo_f(w[i], tag);
-      x[2 * i + 1] = hi_f(w[i], tag);
-    }
-  }
-}
-
-template <typename T>
-__device__ inline Frag8<T> pack8(const float* x) {
-  Frag8<T> f;
-  if constexpr (sizeof(T) == 4) {
-    f.u[0] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                        __float_as_uint(x[3]));
-    f.u[1] = make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]),
-                        __float_as_uint(x[7]));
-  } else {
-    T* tag = nullptr;
-    f.u[0] = make_uint4(pack2(x[0], x[1], tag), pack2(x[2], x[3], tag), pack2(x[4], x[5], tag),
-                        pack2(x[6], x[7], tag));
-  }
-  return f;
-}
-
-// ---- MFMA over an 8-element k-slice per lane -------------------------------
-// A lane in half hh (lanes 32*hh .. 32*hh+31) supplies the 8 k-slots of its
-// half; both operands use the same slot <-> index assignment, so any
-// permutation of the contraction index inside a slice is harmless.
-__device__ inline f32x16 mma8(const Frag8<_Float16>& a, const Frag8<_Float16>& b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a.u[0]),
-                                                __builtin_bit_cast(f16x8, b.u[0]), c, 0, 0, 0);
-}
-__device__ inline f32x16 mma8(const Frag8<__bf16>& a, const Frag8<__bf16>& b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.u[0]),
-                                                 __builtin_bit_cast(bf16x8, b.u[0]), c, 0, 0, 0);
-}
-__device__ inline f32x16 mma8(const Frag8<float>& a, const Frag8<float>& b, f32x16 c) {
-  float av[8], bv[8];
-  unpack8(a, av);
-  unpack8(b, bv);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], c, 0, 0, 0);
-  return c;
-}
-
-// ---- lane maps -------------------------------------------------------------
-// Accumulator register i of a 32x32 MFMA holds row 8*(i/4) + 4*hh + i%4.
-// keymap sends that row to 8*hh + i (i < 8) or 16 + 8*hh + (i - 8) (i >= 8).
-__device__ inline int keymap(int m) {
-  return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-}
-// 16-byte-chunk XOR swizzles: K tile rows (keys) and V^T tile rows (features).
-__device__ inline int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ inline int swz_v(int d) { return (d ^ (d >> 3)) & 7; }
-
-// Exchange with the lane 32 apart; returns {value of lane l, value of lane l^32}
-// in an order that makes max/sum of the pair symmetric across the halves.
-__device__ inline float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <typename T>
-__device__ inline Frag8<T> ld_global8(const char* p) {
-  Frag8<T> f;
-#pragma unroll
-  for (int w = 0; w < Frag8<T>::W; ++w) f.u[w] = *reinterpret_cast<const uint4*>(p + 16 * w);
-  return f;
-}
-template <typename T>
-__device__ inline Frag8<T> zero8() {
-  Frag8<T> f;
-#pragma unroll
-  for (int w = 0; w < Frag8<T>::W; ++w) f.u[w] = make_uint4(0u, 0u, 0u, 0u);
-  return f;
-}
-
-// Per-(dtype, D) tile shape: NQ query waves (32 rows each) x NK key splits,
-// BN keys per wave sub-tile, NBUF LDS buffers.
-template <typename T, int D>
-struct TileCfg {
-  static constexpr bool half = sizeof(T) == 2;
-  static constexpr int NQ = half ? 4 : 1;
-  static constexpr int NK = half ? 1 : (D >= 128 ? 2 : 4);
-  static constexpr int BN = half ? 64 : 32;
-  static constexpr int NBUF = half ? 2 : 1;
-};
 
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool ADD, bool PRENORM>

@@ -1,0 +1,531 @@
+// mha_kernel_half.hpp -- fused masked multi-head attention forward for gfx950
+// (CDNA4), float16 / bfloat16 variant.
+//
+// Sources (web pages, cited by title and section):
+//   [MMHA]  "masked multi head attention" CUDA implementation notes (2kiu.com/news/6063113)
+//   [MAX]   "Why attention must compute the max first" (gsyq.cn/news/340375)
+//   [LNXA]  "How to fuse cross-attention and layer-norm into a single CUDA kernel?"
+//           (cms365.cn question page)
+//
+// Same method as the generic kernel -- S = scale*QK^T, mask before the
+// softmax, online softmax, O += P V with S/P in registers [MAX 2.3, 2.4;
+// MMHA 2] -- arranged for throughput on 16-bit inputs:
+//   * K and V tiles go straight from HBM into LDS with buffer_load ... lds
+//     (16 bytes per lane, no register staging). Rows past Lk come back as
+//     zeros from the buffer's range check, so there are no guards or
+//     branches on the loads. The XOR swizzle is applied by choosing which
+//     global chunk each lane fetches, since the LDS side of these loads is
+//     lane-ordered;
+//   * V stays row-major in LDS and is read transposed with
+//     ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//     (i & 3) of the 8 bytes addressed by lane 4j + (i >> 2) in slot j. With
+//     the addresses chosen below, each lane gets 4 consecutive keys at its own
+//     feature index -- the k-slots of the A operand of O^T = V^T P^T;
+//   * a tile whose keys sit strictly inside every row's legal range runs a
+//     path with no per-element mask tests; only tiles that straddle the
+//     causal diagonal, the padding length or Lk pay for them;
+//   * the running maximum is raised only when a row's new maximum exceeds the
+//     current one by more than 2^8 in probability (8 in log2 units), so the
+//     O rescale is rare; weights of up to 2^8 stay exact in fp32 and are
+//     normalised by the same running sum [MAX 2.3];
+//   * up to two workgroups per CU (launch bound: 2 waves per SIMD) so one
+//     wave's softmax overlaps another's MFMAs.
+#pragma once
+
+#include "mha_common.hpp"
+
+namespace mha {
+
+#define MHA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+typedef __fp16 lds_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+template <typename T>
+__device__ inline uint2 lds_read_tr(const char* p);
+template <>
+__device__ inline uint2 lds_read_tr<_Float16>(const char* p) {
+  return __builtin_bit_cast(uint2,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4f16(MHA_LDS_PTR(lds_f16x4, p)));
+}
+template <>
+__device__ inline uint2 lds_read_tr<__bf16>(const char* p) {
+  return __builtin_bit_cast(uint2,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MHA_LDS_PTR(lds_bf16x4, p)));
+}
+
+// Raw buffer over [base, base + bytes): loads beyond it return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// LDS swizzles, in 16-byte chunks (16 chunks = 64 banks x 4 bytes). A K
+// operand read has 16 lanes hitting 16 different rows at one logical chunk;
+// a transposed V read has 32 lanes hitting 4 consecutive rows x 4 chunks.
+// Both place every lane of such a phase in a distinct chunk slot mod 16.
+template <int CPR>
+__device__ inline int swz_k16(int row) {
+  return CPR >= 16 ? (row & 15) : ((row / (16 / CPR)) & (CPR - 1));
+}
+template <int CPR>
+__device__ inline int swz_v16(int row) {
+  // rows r..r+3 (r % 4 == 0), chunks c..c+3 (c % 4 == 0)
+  if constexpr (CPR >= 16) return 4 * (row & 3);
+  else if constexpr (CPR == 8) return 4 * ((row >> 1) & 1);
+  else return 0;
+}
+
+template <typename T, int D, bool ADD, bool PRENORM>
+__global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
+  static_assert(sizeof(T) == 2, "16-bit element types only");
+  constexpr int E = 2;
+  constexpr int NQ = 4, NT = 256, BM = 128, BN = 64, NB32 = 2;
+  constexpr int NC = D / 16;                  // 16-feature slices of QK^T
+  constexpr int DP = D < 32 ? 32 : D;         // O^T rows, padded to 32
+  constexpr int ND = DP / 32;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int RB = D * E;                   // bytes per K/V row
+  constexpr int TILE_BYTES = BN * RB;
+  constexpr int BUF_BYTES = 2 * TILE_BYTES;   // K tile then V tile
+  constexpr int NCHUNK = BN * CPR;            // multiple of 64
+  constexpr int NLD = (NCHUNK + NT - 1) / NT;
+  constexpr int STAT_BYTES = PRENORM ? NQ * 32 * 8 : 16;
+  constexpr bool SPLIT_P = std::is_same<T, __bf16>::value;
+  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr float RESCALE_GAP = 8.0f;         // log2 units
+  static_assert(NCHUNK % 64 == 0, "tile chunks must fill whole waves");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES + STAT_BYTES];
+  char* const stat_lds = smem + 2 * BUF_BYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+
+  // Workgroup -> work item.
+  //  * causal: every (b, head) of the heaviest query block first, the
+  //    lightest last, in dispatch order (work per block grows with its index);
+  //  * otherwise: consecutive workgroup ids go to different XCDs (8 of them,
+  //    each with its own L2), so ids are remapped to put the query blocks of
+  //    one (b, head group) -- which read the same K/V (and, for pre-LN, the
+  //    same x rows across head groups) -- on one XCD.
+  int b, hg, qblk;
+  {
+    const int G = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
+    const int ngrp = PRENORM ? p.H / p.hg : p.H;
+    int grp;
+    if (p.kind & K_CAUSAL) {
+      grp = bid % (p.B * ngrp);
+      qblk = p.nqblk - 1 - bid / (p.B * ngrp);
+    } else {
+      const int L = (G % 8 == 0) ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+      qblk = L % p.nqblk;
+      grp = L / p.nqblk;
+    }
+    b = grp / ngrp;
+    hg = grp % ngrp;
+  }
+  const int Lq = p.Lq, Lk = p.Lk, H = p.H;
+  const int q0 = qblk * BM;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + n;
+  const bool row_ok = qi < Lq;
+  const bool wave_active = qw0 < Lq;
+  const bool causal = (p.kind & K_CAUSAL) != 0;
+
+  int kpad = Lk;
+  if (p.kind & K_PADDING) {
+    const int L = p.lens[b];
+    kpad = L < 0 ? 0 : (L > Lk ? Lk : L);
+    if ((L < 0 || L > Lk) && hg == 0 && qblk == 0 && tid == 0) atomicOr(p.flags, F_BAD_LENGTH);
+  }
+  int kend_w = kpad;
+  if (causal) kend_w = min(kend_w, min(qw0 + 31, Lq - 1) + 1);
+  if (!wave_active) kend_w = 0;
+  int kend_g = kpad;
+  if (causal) kend_g = min(kend_g, min(q0 + BM - 1, Lq - 1) + 1);
+  const int ntiles = (kend_g + BN - 1) / BN;
+
+  // ---- pre-LN: token statistics, once per workgroup for all its heads ----
+  float2 ms = make_float2(0.f, 0.f);
+  if constexpr (PRENORM) {
+    // token statistics over F = H*D features [LNXA answer step 2]: 16 lanes per
+    // token, 4 tokens per pass, mean then mean squared deviation
+    const int F = H * D;
+    const int nch = F / 8;
+    const int g16 = lane >> 4, l16 = lane & 15;
+    float2* st = reinterpret_cast<float2*>(stat_lds) + wave * 32;
+    for (int r0 = 0; r0 < 32; r0 += 4) {
+      const int row = qw0 + r0 + g16;
+      const bool valid = row < Lq;
+      const char* xr = (const char*)p.x + ((int64_t)b * Lq + (valid ? row : 0)) * (int64_t)F * E;
+      T* tag = nullptr;
+      float s = 0.f;
+      if (valid) {
+        for (int ch = l16; ch < nch; ch += 16) {
+          const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s += lo_f(w[i], tag) + hi_f(w[i], tag);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+      const float mean = s / (float)F;
+      float v2 = 0.f;
+      if (valid) {
+        for (int ch = l16; ch < nch; ch += 16) {
+          const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = lo_f(w[i], tag) - mean, a1 = hi_f(w[i], tag) - mean;
+            v2 += a0 * a0 + a1 * a1;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v2 += __shfl_xor(v2, o, 64);
+      const float rstd = 1.0f / sqrtf(v2 / (float)F + p.eps);
+      if (l16 == 0) st[r0 + g16] = make_float2(mean, rstd);
+    }
+    __syncthreads();
+    ms = st[n];
+  }
+
+  // ---- per-lane constants ----
+  const float c = p.c;
+  int krow_off[NB32], ksw[NB32];
+#pragma unroll
+  for (int blk = 0; blk < NB32; ++blk) {
+    const int row = blk * 32 + keymap(n);
+    krow_off[blk] = row * RB;
+    ksw[blk] = swz_k16<CPR>(row);
+  }
+  // transposed V reads: lane = 16*G + 4*j + r; key = blk*32 + 16*tt + 8*(G>>1) + 4*t + j,
+  // feature = 32*db + 16*(G&1) + 8*(r&1) + 4*(r>>1) (the keymap order of the O^T rows)
+  const int vG = lane >> 4, vj = (lane >> 2) & 3, vr = lane & 3;
+  const int vkey0 = 8 * (vG >> 1) + vj;
+  const int vfeat0 = 16 * (vG & 1) + 8 * (vr & 1) + 4 * (vr >> 1);
+
+  const int nheads = PRENORM ? p.hg : 1;
+  for (int hl = 0; hl < nheads; ++hl) {
+  const int h = PRENORM ? hg * p.hg + hl : hg;
+  const int64_t bh = (int64_t)b * H + h;
+
+  // ---- Q fragments: Q[qi][16c + 8hh + j] (B operand of S^T = K Q^T) ----
+  Frag8<T> qf[NC];
+  if constexpr (!PRENORM) {
+    const char* qrow = (const char*)p.q + ((bh * Lq + (row_ok ? qi : 0)) * D) * E;
+#pragma unroll
+    for (int c2 = 0; c2 < NC; ++c2)
+      qf[c2] = row_ok ? ld_global8<T>(qrow + (16 * c2 + 8 * hh) * E) : zero8<T>();
+  } else {
+    const int F = H * D;
+    const char* xrow = (const char*)p.x + (((int64_t)b * Lq + (row_ok ? qi : 0)) * F + h * D) * E;
+    const char* grow = (const char*)p.gamma + (int64_t)h * D * E;
+    const char* brow = (const char*)p.beta + (int64_t)h * D * E;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int off = (16 * c + 8 * hh) * E;
+      if (!row_ok) { qf[c] = zero8<T>(); continue; }
+      float xv[8], gv[8], bv[8], qv[8];
+      unpack8(ld_global8<T>(xrow + off), xv);
+      unpack8(ld_global8<T>(grow + off), gv);
+      unpack8(ld_global8<T>(brow + off), bv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = (xv[j] - ms.x) * ms.y * gv[j] + bv[j];
+      qf[c] = pack8<T>(qv);
+    }
+  }
+
+  // ---- K/V tiles: HBM -> LDS directly ----
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+  auto issue_tile = [&](int kt0, int buf) {
+    char* kl = smem + buf * BUF_BYTES;
+    char* vl = kl + TILE_BYTES;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int u0 = it * NT + wave * 64;
+      if (NCHUNK % NT != 0 && u0 >= NCHUNK) break;  // whole waves only
+      const int u = u0 + lane;
+      const int row = u / CPR, phys = u % CPR;
+      const uint32_t goff = (uint32_t)(kt0 + row) * RB;
+      const int lck = phys ^ swz_k16<CPR>(row);
+      const int lcv = phys ^ swz_v16<CPR>(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, MHA_LDS_PTR(void, kl + 16 * u0), 16,
+                                               goff + 16 * lck, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 16 * u0), 16,
+                                               goff + 16 * lcv, 0, 0, 0);
+    }
+  };
+
+  // additive mask: raw 16-byte groups for this lane's 2 x NB32 key runs
+  // one buffer per batch entry (wave-uniform); rows past Lq fall outside it
+  const char* addrow = nullptr;
+  __amdgpu_buffer_rsrc_t ars;
+  uint32_t arow_off = 0;
+  if constexpr (ADD) {
+    const char* abase = (const char*)p.add + (int64_t)b * Lq * (int64_t)Lk * E;
+    addrow = abase + (int64_t)(row_ok ? qi : 0) * Lk * E;
+    ars = make_rsrc(abase, (uint32_t)((int64_t)Lq * Lk * E));
+    arow_off = (uint32_t)qi * (uint32_t)Lk * E;
+  }
+  uint4 am_raw[NB32][2], am_nxt[NB32][2];
+  auto load_mask = [&](int kt0, uint4 (&dst)[NB32][2]) {
+#pragma unroll
+    for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int key0 = kt0 + blk * 32 + 16 * g + 8 * hh;
+        if (p.add_vec) {
+          dst[blk][g] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, arow_off + (uint32_t)key0 * E, 0, 0));
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int k0 = key0 + 2 * jj;
+            const uint32_t lo = (row_ok && k0 < Lk) ? reinterpret_cast<const uint16_t*>(addrow)[k0] : 0u;
+            const uint32_t hi =
+                (row_ok && k0 + 1 < Lk) ? reinterpret_cast<const uint16_t*>(addrow)[k0 + 1] : 0u;
+            w[jj] = lo | (hi << 16);
+          }
+          dst[blk][g] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+  };
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  int ncomp = 0;
+
+  if (ntiles > 0) {
+    issue_tile(0, 0);
+    if constexpr (ADD) load_mask(0, am_raw);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
+    __syncthreads();
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt0 = t * BN;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      issue_tile(kt0 + BN, buf ^ 1);
+      if constexpr (ADD) load_mask(kt0 + BN, am_nxt);
+    }
+    const char* kl = smem + buf * BUF_BYTES;
+    const char* vl = kl + TILE_BYTES;
+    const int kb0 = kt0;
+    bool comp = kb0 < kend_w;
+    const bool edge = (kb0 + BN > kpad) || (causal && kb0 + BN - 1 > qw0);
+
+    // additive mask in log2 units, masked entries -inf [MMHA 1: -inf before normalisation]
+    float am[NB32][16];
+    if constexpr (ADD) {
+      float amax = -INFINITY;
+      auto convert = [&](auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+#pragma unroll
+        for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            Frag8<T> f;
+            f.u[0] = am_raw[blk][g];
+            float mv[8];
+            unpack8(f, mv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              float a = mv[j] * LOG2E;  // -inf stays -inf
+              if constexpr (EDGE) {
+                const int key = kb0 + blk * 32 + 16 * g + 8 * hh + j;
+                if (key >= kpad || (causal && key > qi)) a = -INFINITY;
+              }
+              am[blk][8 * g + j] = a;
+              amax = fmaxf(amax, a);
+            }
+          }
+      };
+      if (edge) convert(std::true_type{});
+      else convert(std::false_type{});
+      comp = __ballot(comp && row_ok && amax != -INFINITY) != 0;
+    }
+
+    auto tile = [&](auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
+      // S^T = K Q^T; the two 32-key accumulator chains are interleaved
+      f32x16 s[NB32];
+#pragma unroll
+      for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int blk = 0; blk < NB32; ++blk) {
+          Frag8<T> kf;
+          kf.u[0] = *reinterpret_cast<const uint4*>(kl + krow_off[blk] +
+                                                    16 * ((2 * cc + hh) ^ ksw[blk]));
+          s[blk] = mma8(kf, qf[cc], s[blk]);
+        }
+      // online softmax per 32-key block [MAX 2.3], then O^T += V^T P^T for it,
+      // so one block's exponentials overlap the other block's MFMAs
+#pragma unroll
+      for (int blk = 0; blk < NB32; ++blk) {
+        // ADD: s becomes the log2-unit logit; otherwise s stays raw (scale > 0
+        // commutes with the max) and the scale is applied in the exponent's FMA
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float u = s[blk][i];
+          if constexpr (ADD) {
+            u = __builtin_fmaf(u, c, am[blk][i]);
+          } else if constexpr (EDGE) {
+            const int key = kb0 + blk * 32 + (i < 8 ? 8 * hh + i : 8 + 8 * hh + i);
+            if (key >= kpad || (causal && key > qi)) u = -INFINITY;
+          }
+          s[blk][i] = u;
+          mt = fmaxf(mt, u);
+        }
+        mt = pair_max(mt);
+        if constexpr (!ADD) mt = (mt == -INFINITY) ? -INFINITY : mt * c;
+        // raise the reference maximum only when exceeded by more than the gap
+        if (__ballot(mt > m_run + RESCALE_GAP) != 0) {
+          const float m_new = fmaxf(m_run, mt);
+          const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_fast(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = (ADD || EDGE) ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float e;
+          if constexpr (ADD) {
+            e = exp2_fast(s[blk][i] - m_use);  // -inf -> 0
+          } else {
+            e = exp2_fast(__builtin_fmaf(s[blk][i], c, -m_use));
+            if constexpr (EDGE) e = (s[blk][i] == -INFINITY) ? 0.f : e;  // also when scale = 0
+          }
+          s[blk][i] = e;
+          rs += e;
+        }
+        l_run += rs;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          float pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = s[blk][8 * tt + j];
+          const Frag8<T> pf = pack8<T>(pv);
+          Frag8<T> pf_lo;
+          if constexpr (SPLIT_P) {
+            float hi[8], lo[8];
+            unpack8(pf, hi);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lo[j] = pv[j] - hi[j];
+            pf_lo = pack8<T>(lo);
+          }
+          const int key_a = blk * 32 + 16 * tt + vkey0;  // + 4 for the second read
+          const int sw = swz_v16<CPR>(key_a);            // key_a and key_a + 4 share it
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            const int feat = (32 * db + vfeat0) & (D - 1);
+            const char* a0 = vl + key_a * RB + 16 * ((feat >> 3) ^ sw) + (feat & 7) * E;
+            const uint2 lo4 = lds_read_tr<T>(a0);
+            const uint2 hi4 = lds_read_tr<T>(a0 + 4 * RB);
+            Frag8<T> vf;
+            vf.u[0] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+            o[db] = mma8(vf, pf, o[db]);
+            if constexpr (SPLIT_P) o[db] = mma8(vf, pf_lo, o[db]);
+          }
+        }
+      }
+    };
+
+    if (comp) {
+      ++ncomp;
+      if (edge || ADD) tile(std::true_type{});
+      else tile(std::false_type{});
+    }
+
+    if constexpr (ADD) {
+#pragma unroll
+      for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) am_raw[blk][g] = am_nxt[blk][g];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile is in LDS
+    __syncthreads();
+  }
+
+  if (p.counters && wave_active && lane == 0) {
+    const int nsub = (Lk + BN - 1) / BN;
+    atomicAdd(p.counters + 0, (unsigned long long)ncomp);
+    atomicAdd(p.counters + 1, (unsigned long long)(nsub - ncomp));
+  }
+
+  // ---- epilogue: O / l, residual, flags, 16-byte stores ----
+  const float l_tot = pair_sum(l_run);
+  const bool fully = row_ok && !(l_tot != 0.f);
+  const float inv = (l_tot != 0.f) ? 1.0f / l_tot : 0.f;
+  bool nonfinite = false;
+  if (row_ok) {
+    char* orow;
+    const char* rrow = nullptr;
+    if constexpr (PRENORM) {
+      const int64_t off = (((int64_t)b * Lq + qi) * (H * D) + h * D) * E;
+      orow = (char*)p.out + off;
+      if (p.residual) rrow = (const char*)p.residual + off;
+    } else {
+      orow = (char*)p.out + ((bh * Lq + qi) * D) * E;
+    }
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int d0 = db * 32 + 16 * g + 8 * hh;
+        if (d0 >= D) continue;
+        float ov[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ov[j] = o[db][8 * g + j] * inv;
+        if constexpr (PRENORM) {
+          if (rrow) {
+            float rv[8];
+            unpack8(ld_global8<T>(rrow + d0 * E), rv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ov[j] += rv[j];
+          }
+        }
+        const Frag8<T> f = pack8<T>(ov);
+        float back[8];
+        unpack8(f, back);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) nonfinite |= !__builtin_isfinite(back[j]);
+        *reinterpret_cast<uint4*>(orow + d0 * E) = f.u[0];
+      }
+  }
+  const unsigned long long fm = __ballot(fully && hh == 0);
+  const unsigned long long nf = __ballot(nonfinite);
+  if (lane == 0) {
+    const uint32_t fl = (fm ? F_FULLY_MASKED_ROW : 0u) | (nf ? F_NONFINITE : 0u);
+    if (fl) atomicOr(p.flags, fl);
+    if (p.counters && fm) atomicAdd(p.counters + 2, (unsigned long long)__popcll(fm));
+  }
+  }  // heads of the group
+}
+
+#undef MHA_LDS_PTR
+
+}  // namespace mha

@@ -2,7 +2,8 @@
 // (dtype, D, additive, pre-LN). Included by one translation unit per dtype.
 #pragma once
 
-#include "mha_kernel.hpp"
+#include "mha_kernel_generic.hpp"
+#include "mha_kernel_half.hpp"
 
 namespace mha {
 
@@ -14,11 +15,19 @@ template <typename T, int D, bool ADD, bool PRE>
 hipError_t launch_one(Params p, hipStream_t stream) {
   using Cfg = TileCfg<T, D>;
   p.nqblk = (p.Lq + block_rows<T, D>() - 1) / block_rows<T, D>();
-  const long long grid = (long long)p.B * p.H * p.nqblk;
+  // pre-LN, 16-bit types: one workgroup serves a group of heads of the same
+  // query block, so the token statistics are computed once for the group
+  p.hg = (sizeof(T) == 2 && PRE) ? (p.H % 4 == 0 ? 4 : (p.H % 2 == 0 ? 2 : 1)) : 1;
+  const long long grid = (long long)p.B * (p.H / p.hg) * p.nqblk;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((mha_fwd_kernel<T, D, ADD, PRE>), dim3((unsigned)grid),
-                     dim3(64 * Cfg::NQ * Cfg::NK), 0, stream, p);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((mha_fwd_kernel<T, D, ADD, PRE>), dim3((unsigned)grid),
+                       dim3(64 * Cfg::NQ * Cfg::NK), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
