@@ -76,30 +76,39 @@ __device__ inline int swz_v16(int row) {
   else return 0;
 }
 
-template <typename T, int D, bool ADD, bool PRENORM>
-__global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
+// NK = 1: 4 waves, each 32 query rows against every key tile.
+// NK = 2 (causal masks): 8 waves, two per query group, taking alternate key
+// tiles; the heaviest query block's serial chain halves and one workgroup
+// fills a CU, so the heaviest-first launch order balances the causal
+// triangle. The two partial (m, l, O) states merge through LDS.
+template <typename T, int D, bool ADD, bool PRENORM, int NK>
+__global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p) {
   static_assert(sizeof(T) == 2, "16-bit element types only");
   constexpr int E = 2;
-  constexpr int NQ = 4, NT = 256, BM = 128, BN = 64, NB32 = 2;
+  constexpr int NQ = 4, NW = NQ * NK, NT = 64 * NW, BM = 128, BN = 64, NB32 = 2;
   constexpr int NC = D / 16;                  // 16-feature slices of QK^T
   constexpr int DP = D < 32 ? 32 : D;         // O^T rows, padded to 32
   constexpr int ND = DP / 32;
   constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
   constexpr int RB = D * E;                   // bytes per K/V row
   constexpr int TILE_BYTES = BN * RB;
-  constexpr int BUF_BYTES = 2 * TILE_BYTES;   // K tile then V tile
-  constexpr int NCHUNK = BN * CPR;            // multiple of 64
+  constexpr int SPLIT_BYTES = 2 * TILE_BYTES; // K tile then V tile of one key split
+  constexpr int BUF_BYTES = NK * SPLIT_BYTES;
+  constexpr int NCHUNK = NK * BN * CPR;       // 16-byte chunks per matrix per buffer
   constexpr int NLD = (NCHUNK + NT - 1) / NT;
+  constexpr int MERGE_BYTES = NK > 1 ? NQ * (NK - 1) * 64 * (ND * 16 + 2) * 4 : 0;
+  constexpr int TILE_REGION = 2 * BUF_BYTES > MERGE_BYTES ? 2 * BUF_BYTES : MERGE_BYTES;
   constexpr int STAT_BYTES = PRENORM ? NQ * 32 * 8 : 16;
   constexpr bool SPLIT_P = std::is_same<T, __bf16>::value;
   constexpr float LOG2E = 1.4426950408889634f;
   constexpr float RESCALE_GAP = 8.0f;         // log2 units
   static_assert(NCHUNK % 64 == 0, "tile chunks must fill whole waves");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES + STAT_BYTES];
-  char* const stat_lds = smem + 2 * BUF_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[TILE_REGION + STAT_BYTES];
+  char* const stat_lds = smem + TILE_REGION;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (tid >> 6) % NQ, ks = (tid >> 6) / NQ;  // query group, key split
   const int n = lane & 31, hh = lane >> 5;
 
   // Workgroup -> work item.
@@ -145,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
   if (!wave_active) kend_w = 0;
   int kend_g = kpad;
   if (causal) kend_g = min(kend_g, min(q0 + BM - 1, Lq - 1) + 1);
-  const int ntiles = (kend_g + BN - 1) / BN;
+  const int ntiles = (kend_g + NK * BN - 1) / (NK * BN);
 
   // ---- pre-LN: token statistics, once per workgroup for all its heads ----
   float2 ms = make_float2(0.f, 0.f);
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
     const int nch = F / 8;
     const int g16 = lane >> 4, l16 = lane & 15;
     float2* st = reinterpret_cast<float2*>(stat_lds) + wave * 32;
-    for (int r0 = 0; r0 < 32; r0 += 4) {
+    for (int r0 = 0; r0 < (ks == 0 ? 32 : 0); r0 += 4) {
       const int row = qw0 + r0 + g16;
       const bool valid = row < Lq;
       const char* xr = (const char*)p.x + ((int64_t)b * Lq + (valid ? row : 0)) * (int64_t)F * E;
@@ -245,21 +254,24 @@ __global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
       make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+  const int wid = tid >> 6;  // wave index in the workgroup
   auto issue_tile = [&](int kt0, int buf) {
-    char* kl = smem + buf * BUF_BYTES;
-    char* vl = kl + TILE_BYTES;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
-      const int u0 = it * NT + wave * 64;
+      const int u0 = it * NT + wid * 64;
       if (NCHUNK % NT != 0 && u0 >= NCHUNK) break;  // whole waves only
-      const int u = u0 + lane;
+      const int sp = u0 / (BN * CPR);               // key split of this wave's chunks
+      const int u1 = u0 - sp * (BN * CPR);
+      char* kl = smem + buf * BUF_BYTES + sp * SPLIT_BYTES;
+      char* vl = kl + TILE_BYTES;
+      const int u = u1 + lane;
       const int row = u / CPR, phys = u % CPR;
-      const uint32_t goff = (uint32_t)(kt0 + row) * RB;
+      const uint32_t goff = (uint32_t)(kt0 + sp * BN + row) * RB;
       const int lck = phys ^ swz_k16<CPR>(row);
       const int lcv = phys ^ swz_v16<CPR>(row);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, MHA_LDS_PTR(void, kl + 16 * u0), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, MHA_LDS_PTR(void, kl + 16 * u1), 16,
                                                goff + 16 * lck, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 16 * u0), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 16 * u1), 16,
                                                goff + 16 * lcv, 0, 0, 0);
     }
   };
@@ -310,21 +322,21 @@ __global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
 
   if (ntiles > 0) {
     issue_tile(0, 0);
-    if constexpr (ADD) load_mask(0, am_raw);
+    if constexpr (ADD) load_mask(ks * BN, am_raw);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
     __syncthreads();
   }
 
   for (int t = 0; t < ntiles; ++t) {
-    const int kt0 = t * BN;
+    const int kt0 = t * NK * BN;
     const int buf = t & 1;
     if (t + 1 < ntiles) {
-      issue_tile(kt0 + BN, buf ^ 1);
-      if constexpr (ADD) load_mask(kt0 + BN, am_nxt);
+      issue_tile(kt0 + NK * BN, buf ^ 1);
+      if constexpr (ADD) load_mask(kt0 + NK * BN + ks * BN, am_nxt);
     }
-    const char* kl = smem + buf * BUF_BYTES;
+    const char* kl = smem + buf * BUF_BYTES + ks * SPLIT_BYTES;
     const char* vl = kl + TILE_BYTES;
-    const int kb0 = kt0;
+    const int kb0 = kt0 + ks * BN;  // this wave's 64 keys
     bool comp = kb0 < kend_w;
     const bool edge = (kb0 + BN > kpad) || (causal && kb0 + BN - 1 > qw0);
 
@@ -471,12 +483,53 @@ __global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
   }
 
   if (p.counters && wave_active && lane == 0) {
-    const int nsub = (Lk + BN - 1) / BN;
+    const int nsub = (Lk + BN - 1) / BN;  // key tiles; this split owns those with index % NK == ks
+    const int mine = nsub > ks ? (nsub - ks + NK - 1) / NK : 0;
     atomicAdd(p.counters + 0, (unsigned long long)ncomp);
-    atomicAdd(p.counters + 1, (unsigned long long)(nsub - ncomp));
+    atomicAdd(p.counters + 1, (unsigned long long)(mine - ncomp));
   }
 
-  // ---- epilogue: O / l, residual, flags, 16-byte stores ----
+  // ---- merge the key splits of each query group (log-sum-exp) ----
+  if constexpr (NK > 1) {
+    float* mg = reinterpret_cast<float*>(smem);
+    constexpr int REGS = ND * 16 + 2;
+    if (ks > 0) {
+      float* dst = mg + ((wave * (NK - 1) + (ks - 1)) * REGS) * 64;
+      dst[lane] = m_run;
+      dst[64 + lane] = l_run;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(2 + db * 16 + i) * 64 + lane] = o[db][i];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      float M = m_run;
+#pragma unroll
+      for (int k2 = 1; k2 < NK; ++k2)
+        M = fmaxf(M, mg[((wave * (NK - 1) + (k2 - 1)) * REGS) * 64 + lane]);
+      const float s0 = (M == -INFINITY) ? 0.f : exp2_fast(m_run - M);
+      l_run *= s0;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= s0;
+#pragma unroll
+      for (int k2 = 1; k2 < NK; ++k2) {
+        const float* src = mg + ((wave * (NK - 1) + (k2 - 1)) * REGS) * 64;
+        const float sk = (M == -INFINITY) ? 0.f : exp2_fast(src[lane] - M);
+        l_run += src[64 + lane] * sk;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] += src[(2 + db * 16 + i) * 64 + lane] * sk;
+      }
+    }
+    __syncthreads();  // the merge area is the next head's tile buffer
+  }
+
+  // ---- epilogue (first key split): O / l, residual, flags, 16-byte stores ----
+  if (ks == 0) {
   const float l_tot = pair_sum(l_run);
   const bool fully = row_ok && !(l_tot != 0.f);
   const float inv = (l_tot != 0.f) ? 1.0f / l_tot : 0.f;
@@ -522,6 +575,7 @@ __global__ __launch_bounds__(256, 2) void mha_half_kernel(const Params p) {
     const uint32_t fl = (fm ? F_FULLY_MASKED_ROW : 0u) | (nf ? F_NONFINITE : 0u);
     if (fl) atomicOr(p.flags, fl);
     if (p.counters && fm) atomicAdd(p.counters + 2, (unsigned long long)__popcll(fm));
+  }
   }
   }  // heads of the group
 }

@@ -22,8 +22,12 @@ hipError_t launch_one(Params p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p);
+    if (p.kind & K_CAUSAL)
+      hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE, 2>), dim3((unsigned)grid), dim3(512),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE, 1>), dim3((unsigned)grid), dim3(256),
+                         0, stream, p);
   } else {
     hipLaunchKernelGGL((mha_fwd_kernel<T, D, ADD, PRE>), dim3((unsigned)grid),
                        dim3(64 * Cfg::NQ * Cfg::NK), 0, stream, p);
