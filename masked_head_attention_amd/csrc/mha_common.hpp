@@ -121,14 +121,6 @@ __device__ inline f32x16 mma8(const Frag8<__bf16>& a, const Frag8<__bf16>& b, f3
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.u[0]),
                                                  __builtin_bit_cast(bf16x8, b.u[0]), c, 0, 0, 0);
 }
-__device__ inline f32x16 mma8(const Frag8<float>& a, const Frag8<float>& b, f32x16 c) {
-  float av[8], bv[8];
-  unpack8(a, av);
-  unpack8(b, bv);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], c, 0, 0, 0);
-  return c;
-}
 
 // ---- lane maps -------------------------------------------------------------
 // Accumulator register i of a 32x32 MFMA holds row 8*(i/4) + 4*hh + i%4.
@@ -136,9 +128,6 @@ __device__ inline f32x16 mma8(const Frag8<float>& a, const Frag8<float>& b, f32x
 __device__ inline int keymap(int m) {
   return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
-// 16-byte-chunk XOR swizzles: K tile rows (keys) and V^T tile rows (features).
-__device__ inline int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ inline int swz_v(int d) { return (d ^ (d >> 3)) & 7; }
 
 // Exchange with the lane 32 apart; returns {value of lane l, value of lane l^32}
 // in an order that makes max/sum of the pair symmetric across the halves.
@@ -168,15 +157,13 @@ __device__ inline Frag8<T> zero8() {
   return f;
 }
 
-// Per-(dtype, D) tile shape: NQ query waves (32 rows each) x NK key splits,
-// BN keys per wave sub-tile, NBUF LDS buffers.
-template <typename T, int D>
-struct TileCfg {
-  static constexpr bool half = sizeof(T) == 2;
-  static constexpr int NQ = half ? 4 : 1;
-  static constexpr int NK = half ? 1 : (D >= 128 ? 2 : 4);
-  static constexpr int BN = half ? 64 : 32;
-  static constexpr int NBUF = half ? 2 : 1;
-};
+// LDS address space pointer, for the builtins that take one.
+#define MHA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Raw buffer over [base, base + bytes): loads beyond it return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
 }  // namespace mha

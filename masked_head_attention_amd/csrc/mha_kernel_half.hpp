@@ -36,8 +36,6 @@
 
 namespace mha {
 
-#define MHA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-
 typedef __fp16 lds_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __bf16 lds_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 
@@ -52,12 +50,6 @@ template <>
 __device__ inline uint2 lds_read_tr<__bf16>(const char* p) {
   return __builtin_bit_cast(uint2,
                             __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MHA_LDS_PTR(lds_bf16x4, p)));
-}
-
-// Raw buffer over [base, base + bytes): loads beyond it return zeros.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
 }
 
 // LDS swizzles, in 16-byte chunks (16 chunks = 64 banks x 4 bytes). A K
@@ -579,7 +571,5 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   }
   }  // heads of the group
 }
-
-#undef MHA_LDS_PTR
 
 }  // namespace mha

@@ -2,18 +2,23 @@
 // (dtype, D, additive, pre-LN). Included by one translation unit per dtype.
 #pragma once
 
-#include "mha_kernel_generic.hpp"
+#include "mha_kernel_f32.hpp"
 #include "mha_kernel_half.hpp"
 
 namespace mha {
 
-// Query rows per workgroup and keys per wave tile for (T, D).
+// Query rows per workgroup, and the rows x keys tile of the skip decision.
+//   16-bit types: 128 rows (4 waves x 32), tiles of 32 rows x 64 keys;
+//   float32: 16 rows (NK key-split waves), tiles of 16 rows x 16 keys.
 template <typename T, int D>
-constexpr int block_rows() { return 32 * TileCfg<T, D>::NQ; }
+constexpr int block_rows() { return sizeof(T) == 2 ? 128 : F32Cfg<D>::BM; }
+template <typename T, int D>
+constexpr int skip_rows() { return sizeof(T) == 2 ? 32 : F32Cfg<D>::BM; }
+template <typename T, int D>
+constexpr int skip_keys() { return sizeof(T) == 2 ? 64 : F32Cfg<D>::SUB; }
 
 template <typename T, int D, bool ADD, bool PRE>
 hipError_t launch_one(Params p, hipStream_t stream) {
-  using Cfg = TileCfg<T, D>;
   p.nqblk = (p.Lq + block_rows<T, D>() - 1) / block_rows<T, D>();
   // pre-LN, 16-bit types: one workgroup serves a group of heads of the same
   // query block, so the token statistics are computed once for the group
@@ -29,8 +34,8 @@ hipError_t launch_one(Params p, hipStream_t stream) {
       hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE, 1>), dim3((unsigned)grid), dim3(256),
                          0, stream, p);
   } else {
-    hipLaunchKernelGGL((mha_fwd_kernel<T, D, ADD, PRE>), dim3((unsigned)grid),
-                       dim3(64 * Cfg::NQ * Cfg::NK), 0, stream, p);
+    hipLaunchKernelGGL((mha_f32_kernel<D, ADD, PRE>), dim3((unsigned)grid),
+                       dim3(64 * F32Cfg<D>::NK), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -58,8 +63,8 @@ void tile_shape(int D, int* rows_per_block, int* tile_rows, int* tile_keys) {
 #define MHA_TILE_CASE(DD)                                     \
   case DD:                                                    \
     *rows_per_block = block_rows<T, DD>();                    \
-    *tile_rows = 32;                                          \
-    *tile_keys = TileCfg<T, DD>::BN;                          \
+    *tile_rows = skip_rows<T, DD>();                          \
+    *tile_keys = skip_keys<T, DD>();                          \
     return;
     MHA_TILE_CASE(16)
     MHA_TILE_CASE(32)

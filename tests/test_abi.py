@@ -104,10 +104,11 @@ def test_valid_call_without_gpu_reports_no_device():
 def test_tile_config_and_status_strings():
     lib = _abi.lib()
     r, k = ctypes.c_int(), ctypes.c_int()
-    for dt in (0, 1, 2):
+    # float32: 16 rows x 16 keys (one 16x16x4 MFMA tile); 16-bit: 32 rows x 64 keys
+    for dt, shape in ((0, (16, 16)), (1, (32, 64)), (2, (32, 64))):
         for D in (16, 32, 64, 128):
             assert lib.mha_tile_config(dt, D, 0, ctypes.byref(r), ctypes.byref(k)) == 0
-            assert r.value == 32 and k.value % 32 == 0
+            assert (r.value, k.value) == shape
     assert lib.mha_tile_config(1, 40, 0, ctypes.byref(r), ctypes.byref(k)) == 5
     assert lib.mha_tile_config(7, 64, 0, ctypes.byref(r), ctypes.byref(k)) == 3
     for code, name in _abi.STATUS.items():
