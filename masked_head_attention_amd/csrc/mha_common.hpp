@@ -142,6 +142,11 @@ __device__ inline float pair_sum(float x) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate that waits until at most n vector-memory loads of this
+// wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt at their "no wait" maxima). Loads complete in issue order.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
+
 template <typename T>
 __device__ inline Frag8<T> ld_global8(const char* p) {
   Frag8<T> f;

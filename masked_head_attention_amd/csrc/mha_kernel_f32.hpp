@@ -17,7 +17,7 @@
 // bound the short sequences this type is used for, and the design spreads
 // them over as many SIMDs as possible:
 //   * a workgroup owns 16 query rows and NK waves; wave w takes keys
-//     [32w, 32w + 32) of every NK*32-key tile (two 16-key MFMA tiles), so the
+//     [32w, 32w + 32) of every NK*32-key step (two 16-key MFMA tiles), so the
 //     per-wave chain is a quarter of the row block's work, and a short
 //     sequence fills the chip with B*H*Lq/16 workgroups. The NK partial
 //     (m, l, O) states are merged through LDS by log-sum-exp, each wave
@@ -30,11 +30,14 @@
 //   * Q is pre-multiplied by scale*log2(e), so the scores arrive in log2 units,
 //     exp is v_exp_f32 (2^x) without a further multiply, and a row's maximum
 //     has weight exactly 1;
-//   * K and V tiles go from HBM into LDS with buffer_load ... lds (16 bytes
-//     per lane, no register staging), double-buffered: the next tile's loads
-//     run during this tile's math. Rows past Lk come back as zeros from the
-//     buffer's range check. The first tile is requested before the mask
-//     lengths and Q are read, so their latencies overlap;
+//   * each wave loads exactly the K and V rows it consumes, from HBM into its
+//     own LDS slice with buffer_load ... lds (16 bytes per lane, no register
+//     staging), double-buffered, and waits only on its own loads (vmcnt): the
+//     key loop has no workgroup barrier, K is waited for before V so QK^T
+//     starts while V lands, and a wave whose keys are all masked loads
+//     nothing. Rows past Lk come back as zeros from the buffer's range check.
+//     The first tile is requested before the mask lengths are read, so the
+//     two latencies overlap;
 //   * XOR swizzles on 16-byte chunks keep both LDS read patterns free of bank
 //     conflicts: K is read as 16 rows x one chunk (one b128 per lane), V as 4
 //     rows x 16 consecutive features (one b32 per lane and k-slot);
@@ -77,34 +80,38 @@ template <int D, bool ADD, bool PRENORM>
 __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Params p) {
   using Cfg = F32Cfg<D>;
   constexpr int NK = Cfg::NK, BM = Cfg::BM, BN = Cfg::BN;
-  constexpr int NT = 64 * NK;
-  constexpr int BNT = NK * BN;               // keys per tile
+  constexpr int BNT = NK * BN;               // keys per step of the key loop
   constexpr int E = 4;
   constexpr int CPR = D / 4;                 // 16-byte chunks per K/V row
   constexpr int RB = D * E;                  // bytes per K/V row
   constexpr int NSB = D / 16;                // 16-feature slices: QK^T k-blocks, O^T tiles
-  constexpr int MAT_BYTES = BNT * RB;        // one K or V tile
-  constexpr int BUF_BYTES = 2 * MAT_BYTES;
-  constexpr int NCHUNK = BNT * CPR;          // 16-byte chunks per matrix per tile
-  constexpr int NLD = NCHUNK / NT;           // load instructions per lane per matrix
+  constexpr int MAT_BYTES = BN * RB;         // one wave's K (or V) rows of one step
+  constexpr int WAVE_BYTES = 4 * MAT_BYTES;  // K and V, two buffers
+  constexpr int NLD = MAT_BYTES / 1024;      // 1 KiB load instructions per matrix
+  constexpr int MA = ADD ? 2 : 0;            // additive-mask loads per step
   constexpr int MO_BYTES = NK * NSB * 64 * 16;
+  constexpr int QB = BM * RB;                // Q tile bytes = one wave's merge slot
+  constexpr int NQL = QB / 1024;             // 1 KiB load instructions for Q
+  static_assert(QB == NSB * 64 * 16, "Q tile and merge slot must coincide");
   constexpr int MML_BYTES = NK * 64 * 8;
   constexpr int STAT_BYTES = PRENORM ? BM * 8 : 16;
   constexpr int KM = CPR - 1 < 15 ? CPR - 1 : 15;       // K swizzle mask (chunks)
   constexpr int VM = NSB - 1 < 3 ? NSB - 1 : 3;         // V swizzle mask (4-chunk groups)
   constexpr float LOG2E = 1.4426950408889634f;
-  static_assert(NCHUNK % NT == 0, "tile chunks must fill whole waves");
+  static_assert(MAT_BYTES % 1024 == 0, "a wave's rows must fill whole load instructions");
+  static_assert(NLD + MA + 2 * NLD < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES + MO_BYTES + MML_BYTES + STAT_BYTES];
-  f32x4* const mo = reinterpret_cast<f32x4*>(smem + 2 * BUF_BYTES);
-  float2* const mml = reinterpret_cast<float2*>(smem + 2 * BUF_BYTES + MO_BYTES);
-  float2* const stat = reinterpret_cast<float2*>(smem + 2 * BUF_BYTES + MO_BYTES + MML_BYTES);
+  __shared__ __attribute__((aligned(16))) char smem[NK * WAVE_BYTES + MO_BYTES + MML_BYTES + STAT_BYTES];
+  f32x4* const mo = reinterpret_cast<f32x4*>(smem + NK * WAVE_BYTES);
+  float2* const mml = reinterpret_cast<float2*>(smem + NK * WAVE_BYTES + MO_BYTES);
+  float2* const stat = reinterpret_cast<float2*>(smem + NK * WAVE_BYTES + MO_BYTES + MML_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);  // key split
   const int g = lane >> 4, n = lane & 15;
   const int Lq = p.Lq, Lk = p.Lk, H = p.H;
   const bool causal = (p.kind & K_CAUSAL) != 0;
+  char* const wlds = smem + ks * WAVE_BYTES;  // this wave's K/V buffers
 
   // Workgroup -> (b, h, query block).
   //  * pre-LN: heads fastest, so the workgroups reading the same x rows run
@@ -140,70 +147,76 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   const int q0 = qblk * BM;
   const int qi = q0 + n;
   const bool row_ok = qi < Lq;
+  const float c = p.c;
 
-  // ---- K/V tile 0 requested first: it depends on nothing read below ----
+  // ---- Q tile: HBM -> this wave's merge slot in LDS (free until the merge) ----
+  // Loaded like K (same swizzle) and first, so that every wait for K below
+  // also covers it; rows past Lq come back as zeros.
+  char* const qlds = smem + NK * WAVE_BYTES + ks * QB;
+  if constexpr (!PRENORM) {
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc((const char*)p.q + (bh * Lq + q0) * RB, (uint32_t)(min(Lq - q0, BM) * RB));
+#pragma unroll
+    for (int it = 0; it < NQL; ++it) {
+      const int u = it * 64 + lane;
+      const int row = u / CPR, phys = u % CPR;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MHA_LDS_PTR(void, qlds + 1024 * it), 16,
+                                               (uint32_t)(row * RB + 16 * (phys ^ (row & KM))), 0,
+                                               0, 0);
+    }
+  }
+
+  // ---- this wave's K/V rows and additive-mask entries of a step ----
   const __amdgpu_buffer_rsrc_t krs =
       make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
-  // LDS holds chunk (c ^ swizzle(row)) of a row at position c; the loads are
-  // lane-ordered on the LDS side, so each lane fetches the chunk that belongs
-  // at its position.
-  auto issue_tile = [&](int kt0, int buf) {
-    char* kl = smem + buf * BUF_BYTES;
-    char* vl = kl + MAT_BYTES;
-#pragma unroll
-    for (int it = 0; it < NLD; ++it) {
-      const int u0 = it * NT + ks * 64;
-      const int u = u0 + lane;
-      const int row = u / CPR, phys = u % CPR;
-      const uint32_t goff = (uint32_t)(kt0 + row) * RB;
-      const int lck = phys ^ (row & KM);
-      const int lcv = phys ^ (4 * ((row >> 2) & VM));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, MHA_LDS_PTR(void, kl + 16 * u0), 16,
-                                               goff + 16 * lck, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 16 * u0), 16,
-                                               goff + 16 * lcv, 0, 0, 0);
-    }
-  };
-  issue_tile(0, 0);
-
   // additive mask: 4 consecutive keys per lane and 16-key tile, one buffer per
-  // batch entry (wave-uniform); rows past Lq fall outside it
+  // batch entry (wave-uniform); rows past Lq fall outside it. Loads are
+  // 16 bytes at 4-byte alignment; entries at keys >= Lk (the next row's) are
+  // replaced by -inf when used.
   __amdgpu_buffer_rsrc_t ars;
-  const float* addrow = nullptr;
   uint32_t arow_off = 0;
   if constexpr (ADD) {
     const char* abase = (const char*)p.add + (int64_t)b * Lq * (int64_t)Lk * E;
     ars = make_rsrc(abase, (uint32_t)((int64_t)Lq * Lk * E));
-    addrow = reinterpret_cast<const float*>(abase) + (int64_t)(row_ok ? qi : 0) * Lk;
     arow_off = (uint32_t)qi * (uint32_t)Lk * E;
   }
-  f32x4 am_raw[2], am_nxt[2];
-  auto load_mask = [&](int kt0, f32x4 (&dst)[2]) {
+  f32x4 am_raw[2];
+  // Issue order per step: mask, K, V. LDS holds chunk (c ^ swizzle(row)) of a
+  // row at position c; these loads are lane-ordered on the LDS side, so each
+  // lane fetches the chunk that belongs at its position.
+  auto issue_step = [&](int kb, int buf) {
+    if constexpr (ADD) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key0 = kt0 + ks * BN + 16 * j + 4 * g;
-      if (p.add_vec) {
-        dst[j] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, arow_off + (uint32_t)key0 * E, 0, 0));
-      } else {
+      for (int j = 0; j < 2; ++j)
+        am_raw[j] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ars, arow_off + (uint32_t)(kb + 16 * j + 4 * g) * E, 0, 0));
+    }
+    char* kl = wlds + buf * 2 * MAT_BYTES;
+    char* vl = kl + MAT_BYTES;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[j][r] = (row_ok && key0 + r < Lk) ? addrow[key0 + r] : 0.f;
-      }
+    for (int it = 0; it < NLD; ++it) {
+      const int u = it * 64 + lane;
+      const int row = u / CPR, phys = u % CPR;
+      const uint32_t goff = (uint32_t)(kb + row) * RB + 16 * (phys ^ (row & KM));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, MHA_LDS_PTR(void, kl + 1024 * it), 16, goff, 0,
+                                               0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int u = it * 64 + lane;
+      const int row = u / CPR, phys = u % CPR;
+      const uint32_t goff = (uint32_t)(kb + row) * RB + 16 * (phys ^ (4 * ((row >> 2) & VM)));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 1024 * it), 16, goff, 0,
+                                               0, 0);
     }
   };
-  if constexpr (ADD) load_mask(0, am_raw);
-
-  // ---- Q (B operand of S^T = K Q^T): qf[sb] = c * Q[qi][16sb + 4g .. +3] ----
-  const float c = p.c;
-  f32x4 qf[NSB];
-  if constexpr (!PRENORM) {
-    const float* qrow = (const float*)p.q + (bh * Lq + (row_ok ? qi : 0)) * D;
-    // rows past Lq read row 0 instead; their results are never stored
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) qf[sb] = *reinterpret_cast<const f32x4*>(qrow + 16 * sb + 4 * g) * c;
-  }
+  // Step 0 before the padding length is known: the causal bound alone.
+  const int kend0 = causal ? min(q0 + BM, Lq) : Lk;
+  const bool issued0 = ks * BN < kend0;
+  if (issued0) issue_step(ks * BN, 0);
 
   // ---- key limits (mask decisions that are whole ranges) ----
   int kpad = Lk;
@@ -214,9 +227,17 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   }
   int kend = kpad;  // keys >= kend are masked for every row of the block
   if (causal) kend = min(kend, min(q0 + BM - 1, Lq - 1) + 1);
-  const int ntiles = (kend + BNT - 1) / BNT;
+  const int nsteps = (kend + BNT - 1) / BNT;
 
-  if constexpr (PRENORM) {
+  // ---- Q operand (B of S^T = K Q^T): qf[sb] = c * Q[qi][16sb + 4g .. +3] ----
+  f32x4 qf[NSB];
+  if constexpr (!PRENORM) {
+    if (issued0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(MA + 2 * NLD));  // Q landed
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+      qf[sb] = *reinterpret_cast<const f32x4*>(qlds + n * RB + 16 * ((4 * sb + g) ^ (n & KM))) * c;
+  } else {
     // token statistics over all F = H*D features [LNXA answer step 2]: 16
     // lanes per token, 4 tokens per wave pass, the mean, then the mean squared
     // deviation from it
@@ -278,19 +299,9 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   float m_run = -INFINITY, l_run = 0.f;
   int ncomp = 0;
 
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 (and Q, mask) have landed
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int kt0 = t * BNT;
+  for (int t = 0; t < nsteps; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      issue_tile(kt0 + BNT, buf ^ 1);
-      if constexpr (ADD) load_mask(kt0 + BNT, am_nxt);
-    }
-    const char* kl = smem + buf * BUF_BYTES + ks * BN * RB;  // this wave's 32 K rows
-    const char* vl = smem + buf * BUF_BYTES + MAT_BYTES + ks * BN * RB;
-    const int kb0 = kt0 + ks * BN;  // this wave's first key
+    const int kb0 = t * BNT + ks * BN;  // this wave's first key
     bool comp[2] = {kb0 < kend, kb0 + 16 < kend};
     // some key of the wave's range is masked for some row of the block
     const bool edge = (kb0 + BN > kpad) || (causal && kb0 + BN - 1 > q0);
@@ -313,12 +324,30 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
       }
     }
 
+    // next step's loads for this wave, issued before this step's math
+    const bool nxt = t + 1 < nsteps && kb0 + BNT < kend;
+    if (nxt) issue_step(kb0 + BNT, buf ^ 1);
+
+    const char* kl = wlds + buf * 2 * MAT_BYTES;
+    const char* vl = kl + MAT_BYTES;
+    // wait for this step's K (and everything before it), leaving V and the
+    // next step in flight; then, before P V, for V
+    auto wait_k = [&]() {
+      if (nxt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD + MA + 2 * NLD));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD));
+    };
+    auto wait_v = [&]() {
+      if (nxt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(MA + 2 * NLD));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    };
+
     // NS 16-key tiles starting at tile j0 (NS = 2: both, or the one that has
     // a legal pair); EDGE: some key is masked for some row
     auto tile = [&](auto ns_tag, auto edge_tag, int j0) {
       constexpr int NS = decltype(ns_tag)::value;
       constexpr bool EDGE = decltype(edge_tag)::value;
       // S^T = K Q^T, one accumulator chain per 16-key tile
+      wait_k();
       f32x4 kf[NSB][NS];
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
@@ -335,6 +364,16 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
 #pragma unroll
           for (int j = 0; j < NS; ++j)
             s[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[sb][j][r], qf[sb][r], s[j], 0, 0, 0);
+      // V operands, read while the MFMAs above drain
+      wait_v();
+      float va[NS][4][NSB];
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int fb = 0; fb < NSB; ++fb)
+            va[j][r][fb] = *reinterpret_cast<const float*>(vl + (16 * (j0 + j) + r) * RB + voff[fb]);
       // mask, then the online softmax update [MAX 2.3, 4.2]; scores are in log2 units
       float mt = -INFINITY;
 #pragma unroll
@@ -376,11 +415,8 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int fb = 0; fb < NSB; ++fb) {
-            const float va =
-                *reinterpret_cast<const float*>(vl + (16 * (j0 + j) + r) * RB + voff[fb]);
-            o[fb] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, s[j][r], o[fb], 0, 0, 0);
-          }
+          for (int fb = 0; fb < NSB; ++fb)
+            o[fb] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[j][r][fb], s[j][r], o[fb], 0, 0, 0);
     };
     using One = std::integral_constant<int, 1>;
     using Two = std::integral_constant<int, 2>;
@@ -391,14 +427,8 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
     } else if (comp[0] || comp[1]) {
       tile(One{}, std::true_type{}, comp[0] ? 0 : 1);
     }
-
-    if constexpr (ADD) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) am_raw[j] = am_nxt[j];
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile is in LDS
-    __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load of this wave outlives it
 
   // ---- debug counters: computed / skipped 16x16 tiles of this wave ----
   if (p.counters && lane == 0) {
@@ -417,13 +447,21 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   for (int fb = 0; fb < NSB; ++fb) mo[(ks * NSB + fb) * 64 + lane] = o[fb];
   __syncthreads();
 
-  float M = -INFINITY;
+  constexpr int MINE = (NSB + NK - 1) / NK;  // output slices per wave (some may be empty)
   float2 ml[NK];
+  f32x4 po[MINE][NK];
 #pragma unroll
-  for (int k2 = 0; k2 < NK; ++k2) {
-    ml[k2] = mml[k2 * 64 + lane];
-    M = fmaxf(M, ml[k2].x);
-  }
+  for (int k2 = 0; k2 < NK; ++k2) ml[k2] = mml[k2 * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < MINE; ++i)
+#pragma unroll
+    for (int k2 = 0; k2 < NK; ++k2) {
+      const int fb = ks + i * NK;
+      po[i][k2] = fb < NSB ? mo[(k2 * NSB + fb) * 64 + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k2 = 0; k2 < NK; ++k2) M = fmaxf(M, ml[k2].x);
   float L = 0.f, sk[NK];
 #pragma unroll
   for (int k2 = 0; k2 < NK; ++k2) {
@@ -443,10 +481,13 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   } else {
     orow = (char*)p.out + ((bh * Lq + (row_ok ? qi : 0)) * D) * E;
   }
-  for (int fb = ks; fb < NSB; fb += NK) {
+#pragma unroll
+  for (int i = 0; i < MINE; ++i) {
+    const int fb = ks + i * NK;
+    if (fb >= NSB) break;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k2 = 0; k2 < NK; ++k2) acc += mo[(k2 * NSB + fb) * 64 + lane] * sk[k2];
+    for (int k2 = 0; k2 < NK; ++k2) acc += po[i][k2] * sk[k2];
     acc *= inv;
     const int d0 = 16 * fb + 4 * g;
     if constexpr (PRENORM) {
