@@ -90,9 +90,8 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   constexpr int NLD = MAT_BYTES / 1024;      // 1 KiB load instructions per matrix
   constexpr int MA = ADD ? 2 : 0;            // additive-mask loads per step
   constexpr int MO_BYTES = NK * NSB * 64 * 16;
-  constexpr int QB = BM * RB;                // Q tile bytes = one wave's merge slot
+  constexpr int QB = BM * RB;                // Q tile bytes
   constexpr int NQL = QB / 1024;             // 1 KiB load instructions for Q
-  static_assert(QB == NSB * 64 * 16, "Q tile and merge slot must coincide");
   constexpr int MML_BYTES = NK * 64 * 8;
   constexpr int STAT_BYTES = PRENORM ? BM * 8 : 16;
   constexpr int KM = CPR - 1 < 15 ? CPR - 1 : 15;       // K swizzle mask (chunks)
@@ -101,10 +100,11 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   static_assert(MAT_BYTES % 1024 == 0, "a wave's rows must fill whole load instructions");
   static_assert(NLD + MA + 2 * NLD < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) char smem[NK * WAVE_BYTES + MO_BYTES + MML_BYTES + STAT_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[NK * WAVE_BYTES + MO_BYTES + MML_BYTES + QB + STAT_BYTES];
   f32x4* const mo = reinterpret_cast<f32x4*>(smem + NK * WAVE_BYTES);
   float2* const mml = reinterpret_cast<float2*>(smem + NK * WAVE_BYTES + MO_BYTES);
-  float2* const stat = reinterpret_cast<float2*>(smem + NK * WAVE_BYTES + MO_BYTES + MML_BYTES);
+  char* const qlds = smem + NK * WAVE_BYTES + MO_BYTES + MML_BYTES;
+  float2* const stat = reinterpret_cast<float2*>(qlds + QB);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);  // key split
@@ -149,15 +149,16 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   const bool row_ok = qi < Lq;
   const float c = p.c;
 
-  // ---- Q tile: HBM -> this wave's merge slot in LDS (free until the merge) ----
-  // Loaded like K (same swizzle) and first, so that every wait for K below
-  // also covers it; rows past Lq come back as zeros.
-  char* const qlds = smem + NK * WAVE_BYTES + ks * QB;
+  // ---- Q tile: HBM -> LDS, each wave a share of it ----
+  // Loaded like K (same swizzle) and first, so that a wait that leaves only
+  // this wave's step-0 loads in flight covers it; rows past Lq come back as
+  // zeros. Loads are issued through the compiler-invisible LDS path, so no
+  // compiler-inserted vmcnt wait serialises them with the K/V loads.
   if constexpr (!PRENORM) {
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc((const char*)p.q + (bh * Lq + q0) * RB, (uint32_t)(min(Lq - q0, BM) * RB));
 #pragma unroll
-    for (int it = 0; it < NQL; ++it) {
+    for (int it = ks; it < NQL; it += NK) {
       const int u = it * 64 + lane;
       const int row = u / CPR, phys = u % CPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, MHA_LDS_PTR(void, qlds + 1024 * it), 16,
@@ -232,8 +233,9 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   // ---- Q operand (B of S^T = K Q^T): qf[sb] = c * Q[qi][16sb + 4g .. +3] ----
   f32x4 qf[NSB];
   if constexpr (!PRENORM) {
-    if (issued0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(MA + 2 * NLD));  // Q landed
+    if (issued0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(MA + 2 * NLD));  // this wave's Q share
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();                                                  // everyone's
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
       qf[sb] = *reinterpret_cast<const f32x4*>(qlds + n * RB + 16 * ((4 * sb + g) ^ (n & KM))) * c;
@@ -355,25 +357,29 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
         for (int j = 0; j < NS; ++j)
           kf[sb][j] = *reinterpret_cast<const f32x4*>(kl + 16 * (j0 + j) * RB + koff[sb]);
       f32x4 s[NS];
+      float va[NS][4][NSB];
 #pragma unroll
       for (int j = 0; j < NS; ++j) s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int j = 0; j < NS; ++j)
             s[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[sb][j][r], qf[sb][r], s[j], 0, 0, 0);
-      // V operands, read while the MFMAs above drain
-      wait_v();
-      float va[NS][4][NSB];
+        if (sb == (NSB - 1) / 2) {
+          // V operands, read while the remaining MFMAs run (V lands after K)
+          wait_v();
 #pragma unroll
-      for (int j = 0; j < NS; ++j)
+          for (int j = 0; j < NS; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int fb = 0; fb < NSB; ++fb)
-            va[j][r][fb] = *reinterpret_cast<const float*>(vl + (16 * (j0 + j) + r) * RB + voff[fb]);
+              for (int fb = 0; fb < NSB; ++fb)
+                va[j][r][fb] =
+                    *reinterpret_cast<const float*>(vl + (16 * (j0 + j) + r) * RB + voff[fb]);
+        }
+      }
       // mask, then the online softmax update [MAX 2.3, 4.2]; scores are in log2 units
       float mt = -INFINITY;
 #pragma unroll
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
     sk[k2] = (M == -INFINITY) ? 0.f : exp2_fast(ml[k2].x - M);
     L += ml[k2].y * sk[k2];
   }
-  const float inv = (L != 0.f) ? 1.0f / L : 0.f;
+  const float inv = (L != 0.f) ? __builtin_amdgcn_rcpf(L) : 0.f;  // 1 ulp; exact for L = 1
 
   // ---- epilogue: O / l, pre-LN residual, flags, 16-byte stores ----
   bool nonfinite = false;
