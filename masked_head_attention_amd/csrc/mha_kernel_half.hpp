@@ -92,12 +92,21 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   constexpr int TILE_REGION = 2 * BUF_BYTES > MERGE_BYTES ? 2 * BUF_BYTES : MERGE_BYTES;
   constexpr int STAT_BYTES = PRENORM ? NQ * 32 * 8 : 16;
   constexpr bool SPLIT_P = std::is_same<T, __bf16>::value;
+  // bfloat16: each landed V tile is rewritten once into float16 (exact for
+  // |v| <= 65280; bf16 has 8 significant bits, f16 11), so P V runs as one
+  // f16 MFMA with P in f16 instead of two bf16 MFMAs with P split into hi + lo.
+  // A tile holding a larger finite value falls back to the split. Only where
+  // the extra LDS keeps the occupancy (2 workgroups per CU for NK = 1).
+  constexpr int VC_BYTES = 2 * NK * TILE_BYTES;
+  constexpr bool CONV_V = SPLIT_P && (TILE_REGION + VC_BYTES + STAT_BYTES + 16) <= (NK == 1 ? 80 : 160) * 1024;
   constexpr float LOG2E = 1.4426950408889634f;
   constexpr float RESCALE_GAP = 8.0f;         // log2 units
   static_assert(NCHUNK % 64 == 0, "tile chunks must fill whole waves");
 
-  __shared__ __attribute__((aligned(16))) char smem[TILE_REGION + STAT_BYTES];
-  char* const stat_lds = smem + TILE_REGION;
+  __shared__ __attribute__((aligned(16))) char smem[TILE_REGION + (CONV_V ? VC_BYTES : 0) + STAT_BYTES + 16];
+  char* const vc_lds = smem + TILE_REGION;                              // converted V, [buf][split]
+  char* const stat_lds = smem + TILE_REGION + (CONV_V ? VC_BYTES : 0);
+  int* const vflag = reinterpret_cast<int*>(stat_lds + STAT_BYTES);    // [buf]: tag of a tile that fell back
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (tid >> 6) % NQ, ks = (tid >> 6) / NQ;  // query group, key split
@@ -304,6 +313,33 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       }
   };
 
+  // bf16 -> f16 rewrite of the V tile in buffer b (all key splits), same
+  // swizzled layout; a finite |v| > 65504 marks the tile with `tag`
+  auto convert_v = [&](int b, int tag) {
+    bool big = false;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int u = it * NT + tid;
+      if (NCHUNK % NT != 0 && u >= NCHUNK) break;
+      const int sp = u / (BN * CPR), u1 = u - sp * (BN * CPR);
+      const uint4 x = *reinterpret_cast<const uint4*>(smem + b * BUF_BYTES + sp * SPLIT_BYTES +
+                                                      TILE_BYTES + 16 * u1);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      uint32_t r[4];
+      __bf16* tb = nullptr;
+      _Float16* th = nullptr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = lo_f(w[i], tb), c2 = hi_f(w[i], tb);
+        big |= fmaxf(fabsf(a), fabsf(c2)) > 65504.f;
+        r[i] = pack2(a, c2, th);
+      }
+      *reinterpret_cast<uint4*>(vc_lds + (b * NK + sp) * TILE_BYTES + 16 * u1) =
+          make_uint4(r[0], r[1], r[2], r[3]);
+    }
+    if (__ballot(big) != 0 && lane == 0) vflag[b] = tag;
+  };
+
   f32x16 o[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db)
@@ -315,8 +351,15 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   if (ntiles > 0) {
     issue_tile(0, 0);
     if constexpr (ADD) load_mask(ks * BN, am_raw);
+    if constexpr (CONV_V) {
+      if (hl == 0 && tid < 2) vflag[tid] = -1;
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
     __syncthreads();
+    if constexpr (CONV_V) {
+      convert_v(0, hl << 16);
+      __syncthreads();
+    }
   }
 
   for (int t = 0; t < ntiles; ++t) {
@@ -328,6 +371,8 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     }
     const char* kl = smem + buf * BUF_BYTES + ks * SPLIT_BYTES;
     const char* vl = kl + TILE_BYTES;
+    const char* vcl = vc_lds + (buf * NK + ks) * TILE_BYTES;
+    const bool vconv = CONV_V && vflag[buf] != ((hl << 16) | t);  // f16 copy of V is usable
     const int kb0 = kt0 + ks * BN;  // this wave's 64 keys
     bool comp = kb0 < kend_w;
     const bool edge = (kb0 + BN > kpad) || (causal && kb0 + BN - 1 > qw0);
@@ -432,6 +477,25 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           float pv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) pv[j] = s[blk][8 * tt + j];
+          if constexpr (CONV_V) {
+            if (vconv) {
+              // P and V in float16, one MFMA per 32 features
+              const Frag8<_Float16> ph = pack8<_Float16>(pv);
+              const int key_a = blk * 32 + 16 * tt + vkey0;
+              const int sw = swz_v16<CPR>(key_a);
+#pragma unroll
+              for (int db = 0; db < ND; ++db) {
+                const int feat = (32 * db + vfeat0) & (D - 1);
+                const char* a0 = vcl + key_a * RB + 16 * ((feat >> 3) ^ sw) + (feat & 7) * E;
+                const uint2 lo4 = lds_read_tr<_Float16>(a0);
+                const uint2 hi4 = lds_read_tr<_Float16>(a0 + 4 * RB);
+                Frag8<_Float16> vf;
+                vf.u[0] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+                o[db] = mma8(vf, ph, o[db]);
+              }
+              continue;
+            }
+          }
           const Frag8<T> pf = pack8<T>(pv);
           Frag8<T> pf_lo;
           if constexpr (SPLIT_P) {
@@ -472,6 +536,12 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile is in LDS
     __syncthreads();
+    if constexpr (CONV_V) {
+      if (t + 1 < ntiles) {
+        convert_v(buf ^ 1, (hl << 16) | (t + 1));
+        __syncthreads();
+      }
+    }
   }
 
   if (p.counters && wave_active && lane == 0) {

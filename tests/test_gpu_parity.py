@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import (TOL, assert_parity, from_dev, gather_rows, gpu_inputs, oracle_rows,
-                     run_gpu, run_oracle, sample_rows, to_dev)
+from helpers import (TOL, assert_parity, from_dev, gather_rows, gpu_inputs, half_ulp,
+                     oracle_rows, run_gpu, run_oracle, sample_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -304,3 +304,41 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r}"
+
+
+@pytest.mark.parametrize("kind,D,prenorm", [(0, 64, False), (CAUSAL, 64, False), (0, 64, True),
+                                            (CAUSAL | PADDING, 32, False)])
+def test_bf16_values_beyond_f16_range(kind, D, prenorm):
+    """bfloat16 V is rewritten into float16 for the P V product where it fits;
+    a tile holding a finite value above float16's range (65504) must take the
+    split-P bfloat16 path and still match the oracle. Large values sit in
+    some tiles only, so both paths run in one call."""
+    w = W.make("bf16-big-v", "bf16", B=2, H=2, Lq=150, Lk=300, D=D, kind=kind, seed=5 + D,
+               lens_range=(40, 300) if kind & PADDING else None, prenorm=prenorm, x_mean=0.5,
+               x_std=3.0, residual=prenorm)
+    v = W.bf16_bits_to_f32(w.v).astype(np.float64)
+    v[0, 0, 70, 3] = 3.0e5          # tile 1 of (b0, h0)
+    v[0, 0, 200, D - 1] = -1.0e6    # tile 3 of (b0, h0)
+    v[1, 1, 5, 0] = 7.0e4           # just above float16's largest finite value
+    w.v = W.round_to(v, "bf16")
+    what = f"bf16-big-v-k{kind}-D{D}-pre{int(prenorm)}"
+    print(f"[parity] {what}", flush=True)
+    out_t, flags = run_gpu(w)
+    ref, rflags = run_oracle(w)
+    got = from_dev(out_t)
+    assert flags == rflags
+    assert np.isfinite(got).all()
+    # The bar: tol + half an output ulp, plus 2^-14 * max|V| of the head. With
+    # V up to 1e6 the outputs reach ~1e3, where 2e-3 is below the rounding
+    # noise of any bf16 P V product: P is carried with ~16 significant bits
+    # (hi + lo parts), so a term's error is <= 2^-16 |P_k V_k|; an output near
+    # a bf16 rounding midpoint then lands on either side. A tile that took the
+    # float16 path with such values would give inf or O(|V|) errors instead.
+    vmax = np.abs(w.f64("v")).max(axis=(2, 3))  # [B, H]
+    if prenorm:
+        scale_bh = np.repeat(vmax[:, None, :], w.Lq, axis=1).repeat(w.D, axis=2)  # [B, Lq, H*D]
+    else:
+        scale_bh = vmax[:, :, None, None] * np.ones((1, 1, w.Lq, w.D))
+    err = np.abs(got - ref)
+    allowed = TOL["bf16"] + half_ulp(ref, "bf16") + 2.0 ** -14 * scale_bh
+    assert (err <= allowed).all(), (what, float((err / allowed).max()))
