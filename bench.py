@@ -202,7 +202,9 @@ def cpu_baseline(w: W.Workload, pairs_row: np.ndarray, target_s: float):
             oracle.mha_rows(args["q"], args["k"], args["v"], rows, w.kind, w.lens, add64,
                             w.scale)
 
-    # calibrate on a small sample, then size the timed sample to ~target_s
+    # warm up (thread pool, first touch), calibrate on a small sample, size the
+    # timed sample to ~target_s, then repeat it until target_s has elapsed
+    run(rows_for(min(all_rows, 64))[0])
     n0 = max(64, min(all_rows, 2048))
     rows, b, i = rows_for(n0)
     t0 = time.perf_counter()
@@ -210,14 +212,15 @@ def cpu_baseline(w: W.Workload, pairs_row: np.ndarray, target_s: float):
     t_cal = time.perf_counter() - t0
     per_row = t_cal / len(rows)
     n = int(min(all_rows, max(len(rows), target_s / max(per_row, 1e-9))))
-    reps = 1
-    if n >= all_rows and all_rows * per_row < target_s:
-        reps = max(1, int(target_s / max(all_rows * per_row, 1e-9)))
     rows, b, i = rows_for(n)
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while True:
         run(rows)
-    dt = time.perf_counter() - t0
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
     flops = 4.0 * w.D * float(pairs_row[b, i].sum()) * reps
     return {
         "value": flops / dt / 1e12,
