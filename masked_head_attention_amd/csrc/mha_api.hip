@@ -137,6 +137,7 @@ mha_status run(const Call& c) {
   p.Lk = c.Lk;
   p.kind = c.kind & (MHA_MASK_CAUSAL | MHA_MASK_PADDING);
   p.c = (float)((double)c.scale * 1.4426950408889634);  // log2(e): exp(x) = 2^(x log2 e)
+  p.scale = c.scale;
   p.eps = c.eps;
   p.add_vec = ((int64_t)c.Lk * elem_size(c.dtype)) % 16 == 0;
   p.flags = flags;

@@ -37,6 +37,7 @@ struct Params {
   int hg;                // heads per workgroup (pre-LN kernel of 16-bit types)
   unsigned kind;         // K_CAUSAL | K_PADDING (ADDITIVE is a template switch)
   float c;               // scale * log2(e)
+  float scale;           // scale
   float eps;
   int add_vec;           // additive-mask rows are 16-byte aligned
   uint32_t* flags;

@@ -377,12 +377,24 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     bool comp = kb0 < kend_w;
     const bool edge = (kb0 + BN > kpad) || (causal && kb0 + BN - 1 > qw0);
 
-    // additive mask in log2 units, masked entries -inf [MMHA 1: -inf before normalisation]
+    // additive mask, masked entries -inf [MMHA 1: -inf before normalisation].
+    // Interior tiles keep the raw 16-bit values: the skip is decided on the
+    // bits (a pair equal to two -inf holds no legal key) and each value is
+    // widened inside the FMA that adds it. Edge tiles widen here and apply the
+    // key limits.
     float am[NB32][16];
     if constexpr (ADD) {
-      float amax = -INFINITY;
-      auto convert = [&](auto edge_tag) {
-        constexpr bool EDGE = decltype(edge_tag)::value;
+      bool any = false;
+      if (!edge) {
+        constexpr uint32_t NEG2 = std::is_same<T, __bf16>::value ? 0xFF80FF80u : 0xFC00FC00u;
+#pragma unroll
+        for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const uint4 w = am_raw[blk][g];
+            any |= (w.x != NEG2) | (w.y != NEG2) | (w.z != NEG2) | (w.w != NEG2);
+          }
+      } else {
 #pragma unroll
         for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
@@ -393,19 +405,14 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
             unpack8(f, mv);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              float a = mv[j] * LOG2E;  // -inf stays -inf
-              if constexpr (EDGE) {
-                const int key = kb0 + blk * 32 + 16 * g + 8 * hh + j;
-                if (key >= kpad || (causal && key > qi)) a = -INFINITY;
-              }
+              const int key = kb0 + blk * 32 + 16 * g + 8 * hh + j;
+              const float a = (key >= kpad || (causal && key > qi)) ? -INFINITY : mv[j];
               am[blk][8 * g + j] = a;
-              amax = fmaxf(amax, a);
+              any |= a != -INFINITY;
             }
           }
-      };
-      if (edge) convert(std::true_type{});
-      else convert(std::false_type{});
-      comp = __ballot(comp && row_ok && amax != -INFINITY) != 0;
+      }
+      comp = __ballot(comp && row_ok && any) != 0;
     }
 
     auto tile = [&](auto edge_tag) {
@@ -429,14 +436,23 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       // so one block's exponentials overlap the other block's MFMAs
 #pragma unroll
       for (int blk = 0; blk < NB32; ++blk) {
-        // ADD: s becomes the log2-unit logit; otherwise s stays raw (scale > 0
-        // commutes with the max) and the scale is applied in the exponent's FMA
+        // ADD: s becomes the logit scale*s + mask (natural units); otherwise s
+        // stays raw (scale > 0 commutes with the max) and the scale is applied
+        // in the exponent's FMA
         float mt = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float u = s[blk][i];
           if constexpr (ADD) {
-            u = __builtin_fmaf(u, c, am[blk][i]);
+            float mv;
+            if constexpr (EDGE) {
+              mv = am[blk][i];
+            } else {
+              const uint32_t w = (&am_raw[blk][i >> 3].x)[(i & 7) >> 1];
+              T* tag = nullptr;
+              mv = (i & 1) ? hi_f(w, tag) : lo_f(w, tag);
+            }
+            u = __builtin_fmaf(u, p.scale, mv);
           } else if constexpr (EDGE) {
             const int key = kb0 + blk * 32 + (i < 8 ? 8 * hh + i : 8 + 8 * hh + i);
             if (key >= kpad || (causal && key > qi)) u = -INFINITY;
@@ -445,7 +461,8 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           mt = fmaxf(mt, u);
         }
         mt = pair_max(mt);
-        if constexpr (!ADD) mt = (mt == -INFINITY) ? -INFINITY : mt * c;
+        if constexpr (ADD) mt *= LOG2E;  // to log2 units
+        else mt = (mt == -INFINITY) ? -INFINITY : mt * c;
         // raise the reference maximum only when exceeded by more than the gap
         if (__ballot(mt > m_run + RESCALE_GAP) != 0) {
           const float m_new = fmaxf(m_run, mt);
@@ -463,7 +480,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
         for (int i = 0; i < 16; ++i) {
           float e;
           if constexpr (ADD) {
-            e = exp2_fast(s[blk][i] - m_use);  // -inf -> 0
+            e = exp2_fast(__builtin_fmaf(s[blk][i], LOG2E, -m_use));  // -inf -> 0
           } else {
             e = exp2_fast(__builtin_fmaf(s[blk][i], c, -m_use));
             if constexpr (EDGE) e = (s[blk][i] == -INFINITY) ? 0.f : e;  // also when scale = 0
@@ -524,7 +541,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 
     if (comp) {
       ++ncomp;
-      if (edge || ADD) tile(std::true_type{});
+      if (edge) tile(std::true_type{});
       else tile(std::false_type{});
     }
 
