@@ -49,6 +49,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read through a native vector type. The compiler keeps precise
+// memory-operand information for it; a read of HIP's uint4 struct is treated
+// as possibly overlapping every direct-to-LDS load still in flight, and gets
+// an s_waitcnt vmcnt(0) in front of it.
+__device__ inline uint4 lds_load16(const char* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Eight consecutive elements of type T, as raw 16-byte words.
 template <typename T>

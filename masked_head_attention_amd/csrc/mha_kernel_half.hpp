@@ -322,8 +322,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       const int u = it * NT + tid;
       if (NCHUNK % NT != 0 && u >= NCHUNK) break;
       const int sp = u / (BN * CPR), u1 = u - sp * (BN * CPR);
-      const uint4 x = *reinterpret_cast<const uint4*>(smem + b * BUF_BYTES + sp * SPLIT_BYTES +
-                                                      TILE_BYTES + 16 * u1);
+      const uint4 x = lds_load16(smem + b * BUF_BYTES + sp * SPLIT_BYTES + TILE_BYTES + 16 * u1);
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
       uint32_t r[4];
       __bf16* tb = nullptr;
@@ -428,8 +427,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
         for (int blk = 0; blk < NB32; ++blk) {
           Frag8<T> kf;
-          kf.u[0] = *reinterpret_cast<const uint4*>(kl + krow_off[blk] +
-                                                    16 * ((2 * cc + hh) ^ ksw[blk]));
+          kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
           s[blk] = mma8(kf, qf[cc], s[blk]);
         }
       // online softmax per 32-key block [MAX 2.3], then O^T += V^T P^T for it,
