@@ -414,8 +414,14 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       comp = __ballot(comp && row_ok && any) != 0;
     }
 
-    auto tile = [&](auto edge_tag) {
+    // One 64-key tile. EDGE: per-element key limits (causal diagonal,
+    // padding length, Lk); VCONV: P V from the float16 copy of V. Both are
+    // uniform over the workgroup, so the body below has a single branch (the
+    // rare rescale) and the scheduler can run one 32-key block's
+    // exponentials under the other block's MFMAs.
+    auto tile = [&](auto edge_tag, auto vconv_tag) {
       constexpr bool EDGE = decltype(edge_tag)::value;
+      constexpr bool VCONV = decltype(vconv_tag)::value;
       // S^T = K Q^T; the two 32-key accumulator chains are interleaved
       f32x16 s[NB32];
 #pragma unroll
@@ -430,14 +436,12 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
           s[blk] = mma8(kf, qf[cc], s[blk]);
         }
-      // online softmax per 32-key block [MAX 2.3], then O^T += V^T P^T for it,
-      // so one block's exponentials overlap the other block's MFMAs
+      // online softmax over the tile [MAX 2.3]. ADD: s becomes the logit
+      // scale*s + mask (natural units); otherwise s stays raw (scale > 0
+      // commutes with the max) and the scale is applied in the exponent's FMA
+      float mt = -INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < NB32; ++blk) {
-        // ADD: s becomes the logit scale*s + mask (natural units); otherwise s
-        // stays raw (scale > 0 commutes with the max) and the scale is applied
-        // in the exponent's FMA
-        float mt = -INFINITY;
+      for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float u = s[blk][i];
@@ -458,22 +462,24 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           s[blk][i] = u;
           mt = fmaxf(mt, u);
         }
-        mt = pair_max(mt);
-        if constexpr (ADD) mt *= LOG2E;  // to log2 units
-        else mt = (mt == -INFINITY) ? -INFINITY : mt * c;
-        // raise the reference maximum only when exceeded by more than the gap
-        if (__ballot(mt > m_run + RESCALE_GAP) != 0) {
-          const float m_new = fmaxf(m_run, mt);
-          const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_fast(m_run - m_new);
-          l_run *= alpha;
+      mt = pair_max(mt);
+      if constexpr (ADD) mt *= LOG2E;  // to log2 units
+      else mt = (mt == -INFINITY) ? -INFINITY : mt * c;
+      // raise the reference maximum only when exceeded by more than the gap
+      if (__ballot(mt > m_run + RESCALE_GAP) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-          m_run = m_new;
-        }
-        const float m_use = (ADD || EDGE) ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
-        float rs = 0.f;
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (ADD || EDGE) ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float e;
@@ -486,61 +492,66 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           s[blk][i] = e;
           rs += e;
         }
-        l_run += rs;
+      l_run += rs;
+      // O^T += V^T P^T, 16 keys per MFMA k-step
+#pragma unroll
+      for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           float pv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) pv[j] = s[blk][8 * tt + j];
-          if constexpr (CONV_V) {
-            if (vconv) {
-              // P and V in float16, one MFMA per 32 features
-              const Frag8<_Float16> ph = pack8<_Float16>(pv);
-              const int key_a = blk * 32 + 16 * tt + vkey0;
-              const int sw = swz_v16<CPR>(key_a);
-#pragma unroll
-              for (int db = 0; db < ND; ++db) {
-                const int feat = (32 * db + vfeat0) & (D - 1);
-                const char* a0 = vcl + key_a * RB + 16 * ((feat >> 3) ^ sw) + (feat & 7) * E;
-                const uint2 lo4 = lds_read_tr<_Float16>(a0);
-                const uint2 hi4 = lds_read_tr<_Float16>(a0 + 4 * RB);
-                Frag8<_Float16> vf;
-                vf.u[0] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
-                o[db] = mma8(vf, ph, o[db]);
-              }
-              continue;
-            }
-          }
-          const Frag8<T> pf = pack8<T>(pv);
-          Frag8<T> pf_lo;
-          if constexpr (SPLIT_P) {
-            float hi[8], lo[8];
-            unpack8(pf, hi);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) lo[j] = pv[j] - hi[j];
-            pf_lo = pack8<T>(lo);
-          }
           const int key_a = blk * 32 + 16 * tt + vkey0;  // + 4 for the second read
           const int sw = swz_v16<CPR>(key_a);            // key_a and key_a + 4 share it
+          if constexpr (VCONV) {
+            // P and V in float16, one MFMA per 32 features
+            const Frag8<_Float16> ph = pack8<_Float16>(pv);
 #pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const int feat = (32 * db + vfeat0) & (D - 1);
-            const char* a0 = vl + key_a * RB + 16 * ((feat >> 3) ^ sw) + (feat & 7) * E;
-            const uint2 lo4 = lds_read_tr<T>(a0);
-            const uint2 hi4 = lds_read_tr<T>(a0 + 4 * RB);
-            Frag8<T> vf;
-            vf.u[0] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
-            o[db] = mma8(vf, pf, o[db]);
-            if constexpr (SPLIT_P) o[db] = mma8(vf, pf_lo, o[db]);
+            for (int db = 0; db < ND; ++db) {
+              const int feat = (32 * db + vfeat0) & (D - 1);
+              const char* a0 = vcl + key_a * RB + 16 * ((feat >> 3) ^ sw) + (feat & 7) * E;
+              const uint2 lo4 = lds_read_tr<_Float16>(a0);
+              const uint2 hi4 = lds_read_tr<_Float16>(a0 + 4 * RB);
+              Frag8<_Float16> vf;
+              vf.u[0] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+              o[db] = mma8(vf, ph, o[db]);
+            }
+          } else {
+            const Frag8<T> pf = pack8<T>(pv);
+            Frag8<T> pf_lo;
+            if constexpr (SPLIT_P) {
+              float hi[8], lo[8];
+              unpack8(pf, hi);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) lo[j] = pv[j] - hi[j];
+              pf_lo = pack8<T>(lo);
+            }
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+              const int feat = (32 * db + vfeat0) & (D - 1);
+              const char* a0 = vl + key_a * RB + 16 * ((feat >> 3) ^ sw) + (feat & 7) * E;
+              const uint2 lo4 = lds_read_tr<T>(a0);
+              const uint2 hi4 = lds_read_tr<T>(a0 + 4 * RB);
+              Frag8<T> vf;
+              vf.u[0] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+              o[db] = mma8(vf, pf, o[db]);
+              if constexpr (SPLIT_P) o[db] = mma8(vf, pf_lo, o[db]);
+            }
           }
         }
-      }
     };
 
     if (comp) {
       ++ncomp;
-      if (edge) tile(std::true_type{});
-      else tile(std::false_type{});
+      using TT = std::true_type;
+      using FF = std::false_type;
+      if (CONV_V && vconv) {
+        if (edge) tile(TT{}, std::integral_constant<bool, CONV_V>{});
+        else tile(FF{}, std::integral_constant<bool, CONV_V>{});
+      } else {
+        if (edge) tile(TT{}, FF{});
+        else tile(FF{}, FF{});
+      }
     }
 
     if constexpr (ADD) {
