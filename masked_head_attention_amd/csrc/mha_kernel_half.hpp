@@ -560,14 +560,16 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
         for (int g = 0; g < 2; ++g) am_raw[blk][g] = am_nxt[blk][g];
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile is in LDS
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's share of the next tile is in LDS
     if constexpr (CONV_V) {
-      if (t + 1 < ntiles) {
-        convert_v(buf ^ 1, (hl << 16) | (t + 1));
-        __syncthreads();
-      }
+      // each thread rewrites exactly the V chunks it loaded itself, so its own
+      // wait suffices; the barrier below publishes the copy with the tile.
+      // Nothing reads buffer buf ^ 1 any more: its last readers (tile t - 1)
+      // passed the previous barrier.
+      asm volatile("" ::: "memory");
+      if (t + 1 < ntiles) convert_v(buf ^ 1, (hl << 16) | (t + 1));
     }
+    __syncthreads();
   }
 
   if (p.counters && wave_active && lane == 0) {
