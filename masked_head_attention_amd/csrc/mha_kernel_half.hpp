@@ -88,7 +88,13 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   constexpr int BUF_BYTES = NK * SPLIT_BYTES;
   constexpr int NCHUNK = NK * BN * CPR;       // 16-byte chunks per matrix per buffer
   constexpr int NLD = (NCHUNK + NT - 1) / NT;
-  constexpr int MERGE_BYTES = NK > 1 ? NQ * (NK - 1) * 64 * (ND * 16 + 2) * 4 : 0;
+  // two key splits (NK = 2): each wave finishes half of the 32-feature O
+  // blocks and hands the other half, with its (m, l), to its partner
+  constexpr int HALF = ND / 2;
+  constexpr bool SPLIT_FINISH = NK == 2 && ND >= 2;
+  constexpr int PART_BYTES = 64 * 8 + HALF * 4 * 64 * 16;  // (m, l) + HALF blocks of 16 floats, per lane
+  constexpr int MERGE_BYTES = SPLIT_FINISH ? NQ * NK * PART_BYTES
+                              : NK > 1 ? NQ * (NK - 1) * 64 * (ND * 16 + 2) * 4 : 0;
   constexpr int TILE_REGION = 2 * BUF_BYTES > MERGE_BYTES ? 2 * BUF_BYTES : MERGE_BYTES;
   constexpr int STAT_BYTES = PRENORM ? NQ * 32 * 8 : 16;
   constexpr bool SPLIT_P = std::is_same<T, __bf16>::value;
@@ -580,7 +586,49 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   }
 
   // ---- merge the key splits of each query group (log-sum-exp) ----
-  if constexpr (NK > 1) {
+  if constexpr (SPLIT_FINISH) {
+    // wave (w, ks) finishes O blocks [ks*HALF, ks*HALF + HALF) and hands the
+    // others to (w, ks^1); both combine the two states in the same order
+    // (split 0's terms first), so the halves of a row share one l
+    char* const out_part = smem + (wave * NK + ks) * PART_BYTES;
+    const char* const in_part = smem + (wave * NK + (ks ^ 1)) * PART_BYTES;
+    auto merge = [&](auto ks_c) {
+      constexpr int KS = decltype(ks_c)::value;
+      constexpr int GIVE = (KS ^ 1) * HALF, KEEP = KS * HALF;
+      reinterpret_cast<float2*>(out_part)[lane] = make_float2(m_run, l_run);
+      float4* const po = reinterpret_cast<float4*>(out_part + 512);
+#pragma unroll
+      for (int hb = 0; hb < HALF; ++hb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          po[(hb * 4 + q) * 64 + lane] = make_float4(o[GIVE + hb][4 * q], o[GIVE + hb][4 * q + 1],
+                                                     o[GIVE + hb][4 * q + 2], o[GIVE + hb][4 * q + 3]);
+      __syncthreads();
+      const float2 ml = reinterpret_cast<const float2*>(in_part)[lane];
+      const float m0 = KS == 0 ? m_run : ml.x, m1 = KS == 0 ? ml.x : m_run;
+      const float l0 = KS == 0 ? l_run : ml.y, l1 = KS == 0 ? ml.y : l_run;
+      const float M = fmaxf(m0, m1);
+      const float s0 = (M == -INFINITY) ? 0.f : exp2_fast(m0 - M);
+      const float s1 = (M == -INFINITY) ? 0.f : exp2_fast(m1 - M);
+      l_run = l0 * s0 + l1 * s1;
+      const float4* const pi = reinterpret_cast<const float4*>(in_part + 512);
+#pragma unroll
+      for (int hb = 0; hb < HALF; ++hb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = pi[(hb * 4 + q) * 64 + lane];
+          const float g[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = o[KEEP + hb][4 * q + r];
+            o[KEEP + hb][4 * q + r] = KS == 0 ? x * s0 + g[r] * s1 : g[r] * s0 + x * s1;
+          }
+        }
+    };
+    if (ks == 0) merge(std::integral_constant<int, 0>{});
+    else merge(std::integral_constant<int, 1>{});
+    __syncthreads();  // the merge area is the next head's tile buffer
+  } else if constexpr (NK > 1) {
     float* mg = reinterpret_cast<float*>(smem);
     constexpr int REGS = ND * 16 + 2;
     if (ks > 0) {
@@ -618,8 +666,12 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     __syncthreads();  // the merge area is the next head's tile buffer
   }
 
-  // ---- epilogue (first key split): O / l, residual, flags, 16-byte stores ----
-  if (ks == 0) {
+  // ---- epilogue: O / l, residual, flags, 16-byte stores. With two key
+  // splits each wave stores the O blocks it finished; otherwise the first
+  // split stores them all ----
+  const int db_lo = SPLIT_FINISH ? ks * HALF : 0;
+  const int db_hi = SPLIT_FINISH ? db_lo + HALF : ND;
+  if (SPLIT_FINISH || ks == 0) {
   const float l_tot = pair_sum(l_run);
   const bool fully = row_ok && !(l_tot != 0.f);
   const float inv = (l_tot != 0.f) ? 1.0f / l_tot : 0.f;
@@ -639,7 +691,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int d0 = db * 32 + 16 * g + 8 * hh;
-        if (d0 >= D) continue;
+        if (d0 >= D || db < db_lo || db >= db_hi) continue;
         float ov[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) ov[j] = o[db][8 * g + j] * inv;
@@ -659,7 +711,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
         *reinterpret_cast<uint4*>(orow + d0 * E) = f.u[0];
       }
   }
-  const unsigned long long fm = __ballot(fully && hh == 0);
+  const unsigned long long fm = __ballot(fully && hh == 0 && ks == 0);  // one split reports rows
   const unsigned long long nf = __ballot(nonfinite);
   if (lane == 0) {
     const uint32_t fl = (fm ? F_FULLY_MASKED_ROW : 0u) | (nf ? F_NONFINITE : 0u);

@@ -108,7 +108,13 @@ def test_workload_full_size_sampled(cfg):
 
 # ---- exact decisions: skip counters and the mask probe ---------------------
 @pytest.mark.parametrize("cfg,over", [(2, {}), (3, dict(H=2, Lq=700, Lk=700)),
-                                      (5, dict(B=4, H=2)), (1, {})])
+                                      (5, dict(B=4, H=2)), (1, {}),
+                                      # 16-bit causal runs two key splits per query
+                                      # block; zero lengths make fully masked rows
+                                      (3, dict(B=3, H=2, Lq=300, Lk=300, D=64,
+                                               kind=CAUSAL | PADDING, lens_range=(0, 2))),
+                                      (3, dict(B=2, H=2, Lq=260, Lk=260, D=128, dtype="bf16",
+                                               kind=CAUSAL | PADDING, lens_range=(0, 1)))])
 def test_skip_counters_match_oracle(cfg, over):
     import torch
     import masked_head_attention_amd as M
