@@ -52,6 +52,16 @@ __device__ inline uint2 lds_read_tr<__bf16>(const char* p) {
                             __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MHA_LDS_PTR(lds_bf16x4, p)));
 }
 
+// Sum of the eight float16 values in w, added to acc in float32 (v_dot2 with
+// (1, 1): each product is exact).
+__device__ inline float row_sum_f16x8(const uint4 w, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.z), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), one, acc, false);
+}
+
 // LDS swizzles, in 16-byte chunks (16 chunks = 64 banks x 4 bytes). A K
 // operand read has 16 lanes hitting 16 different rows at one logical chunk;
 // a transposed V read has 32 lanes hitting 4 consecutive rows x 4 chunks.
@@ -483,6 +493,10 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
         m_run = m_new;
       }
       const float m_use = (ADD || EDGE) ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
+      // P in float16 (f16 inputs, or bf16 with the float16 V copy): the row
+      // sum is taken from the packed P the MFMA consumes, two weights per
+      // v_dot2 with float32 accumulation
+      constexpr bool SUM_PACKED = VCONV || !SPLIT_P;
       float rs = 0.f;
 #pragma unroll
       for (int blk = 0; blk < NB32; ++blk)
@@ -496,9 +510,8 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
             if constexpr (EDGE) e = (s[blk][i] == -INFINITY) ? 0.f : e;  // also when scale = 0
           }
           s[blk][i] = e;
-          rs += e;
+          if constexpr (!SUM_PACKED) rs += e;
         }
-      l_run += rs;
       // O^T += V^T P^T, 16 keys per MFMA k-step
 #pragma unroll
       for (int blk = 0; blk < NB32; ++blk)
@@ -512,6 +525,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           if constexpr (VCONV) {
             // P and V in float16, one MFMA per 32 features
             const Frag8<_Float16> ph = pack8<_Float16>(pv);
+            rs = row_sum_f16x8(ph.u[0], rs);
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
               const int feat = (32 * db + vfeat0) & (D - 1);
@@ -524,6 +538,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
             }
           } else {
             const Frag8<T> pf = pack8<T>(pv);
+            if constexpr (SUM_PACKED) rs = row_sum_f16x8(pf.u[0], rs);
             Frag8<T> pf_lo;
             if constexpr (SPLIT_P) {
               float hi[8], lo[8];
@@ -545,6 +560,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
             }
           }
         }
+      l_run += rs;
     };
 
     if (comp) {
