@@ -10,8 +10,10 @@ host's launch rate; the eager (launch-per-call) time is reported beside it.
 
 Prints one JSON line: metric, value (effective TFLOP/s, masked-out work not
 counted), us_per_call, the roofline of the kernel and the fp64 CPU oracle's
-rate on the host cores (cpu_baseline). ``--config N`` picks workload N
-(default 2: fp32 B=4 H=8 L=128 D=64, causal + key padding).
+rate on the host cores (cpu_baseline). For HBM-bound workloads a cold-cache
+figure is added (cold_cache): the median per-call time with the caches flushed
+before each call. ``--config N`` picks workload N (default 2: fp32 B=4 H=8
+L=128 D=64, causal + key padding).
 """
 from __future__ import annotations
 
@@ -85,16 +87,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel sources; else None."""
+def stored_counter(workload: str, key: str = "hbm_bytes_per_launch"):
+    """A per-launch figure (HBM bytes, executed MFMA FLOPs) from a committed
+    rocprofv3 --pmc summary, if it was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         txt = f.read()
     m = re.search(r"^kernel_sources_sha256_16:\s*(\S+)", txt, re.M)
-    t = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    t = re.search(r"^" + re.escape(key) + r":\s*([0-9.eE+]+)", txt, re.M)
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
@@ -165,6 +168,27 @@ def time_gpu(step, K: int, Wm: int, eager: bool):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) * 1e-3 / K
+
+
+def time_cold(step, calls: int, flush_mib: int = 512):
+    """Median seconds per call with the caches cold: before each call a fill
+    kernel writes flush_mib MiB on the same stream (more than the 256 MB
+    Infinity Cache and the L2s hold), then the call alone is timed between HIP
+    events. Per-call events include the launch gap, which graph replay hides."""
+    import torch
+
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for _ in range(calls + 1):  # the first call is untimed
+        buf.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        step()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) * 1e-3)
+    del buf
+    return float(np.median(times[1:]))
 
 
 # ---------------------------------------------------------------------------
@@ -243,6 +267,9 @@ def main(argv=None):
     ap.add_argument("--eager", action="store_true",
                     help="time launch-per-call steps instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing of HBM-bound workloads")
+    ap.add_argument("--cold-calls", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration)")
@@ -287,7 +314,18 @@ def main(argv=None):
         roof = {"bound": "hbm", "achieved": alg_bytes / t_step / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(w.name)
+    roof["traffic"] = stored_counter(w.name)
+    executed = stored_counter(w.name, "executed_mfma_flops_per_launch")
+    if executed is not None and roof["bound"] == "mfma":
+        # executed MFMA work includes masked entries inside computed tiles
+        roof["executed_mfma_frac"] = executed / t_step / 1e12 / PEAK_TFLOPS[w.dtype]
+    cold = None
+    if roof["bound"] == "hbm" and not args.no_cold:
+        t_cold = time_cold(step, args.cold_calls)
+        cold = {"us_per_call": t_cold * 1e6, "calls": args.cold_calls, "flush_mib": 512,
+                "achieved": alg_bytes / t_cold / 1e9, "unit": "GB/s",
+                "frac": alg_bytes / t_cold / 1e9 / PEAK_HBM_GBS,
+                "timing": "median of per-call HIP events, caches flushed before each call"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -304,7 +342,8 @@ def main(argv=None):
         "warmup": args.warmup, "ms_per_step": t_step * 1e3, "us_per_call": t_step * 1e6,
         "eager_us_per_call": t_eager * 1e6, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded, workloads.py recipe)",
-        "config": cfg, "roofline": roof, "cpu_baseline": cpu, "device_flags": flags,
+        "config": cfg, "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu,
+        "device_flags": flags,
         "kernel_sources_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line))
