@@ -287,10 +287,17 @@ def main(argv=None):
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        dst.copy_(src)  # untimed first copy
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
         for _ in range(5):
             dst.copy_(src)
+        e.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+        sec = s.elapsed_time(e) * 1e-3 / 5
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 6,
+                          "us_per_copy": sec * 1e6, "hbm_GBs_read_plus_write": 2 * n * 4 / sec / 1e9}))
         return 0
 
     import masked_head_attention_amd as M
