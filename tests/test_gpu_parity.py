@@ -81,6 +81,33 @@ def test_prenorm_sweep(dtype, kind):
     _check(w, f"prenorm-{dtype}-k{kind}")
 
 
+def _random_shapes(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        dtype = ["f32", "f16", "bf16"][c % 3]
+        D = [16, 32, 64, 128][int(rng.integers(4))]
+        kind = KINDS[int(rng.integers(len(KINDS)))]
+        prenorm = bool(c % 4 == 3) and not (kind & ADDITIVE and kind & CAUSAL)
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        Lq, Lk = int(rng.integers(1, 260)), int(rng.integers(1, 260))
+        if c % 5 == 0:
+            Lq, Lk = max(Lq, Lk), min(Lq, Lk)  # more queries than keys
+        cases.append((dtype, D, kind, prenorm, B, H, Lq, Lk, 100 + c))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,D,kind,prenorm,B,H,Lq,Lk,seed", _random_shapes())
+def test_random_shapes(dtype, D, kind, prenorm, B, H, Lq, Lk, seed):
+    """Seeded random shapes: Lq > Lk with causal, single heads, two- and
+    three-head pre-LN groups, lengths of 1."""
+    w = W.make("rand", dtype, B=B, H=H, Lq=Lq, Lk=Lk, D=D, kind=kind, seed=seed,
+               lens_range=(0, Lk) if kind & (PADDING | ADDITIVE) else None,
+               block_p=0.2 if kind & ADDITIVE else 0.0, block=16, prenorm=prenorm,
+               x_mean=0.5, x_std=2.0, residual=prenorm)
+    _check(w, f"rand-{dtype}-D{D}-k{kind}-pre{int(prenorm)}-{B}x{H}x{Lq}x{Lk}")
+
+
 def test_unaligned_additive_rows():
     """Lk * 2 bytes not a multiple of 16: the additive mask rows are read
     element by element."""
