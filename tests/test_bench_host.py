@@ -1,0 +1,49 @@
+"""Host-side accounting of bench.py (no GPU): effective FLOPs are 4*D times the
+legal (b, h, i, j) pairs the oracle counts; algorithmic bytes follow their
+definition; the multi-GPU request is refused with a message."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads as W
+
+
+@pytest.mark.parametrize("cfg,over", [(1, {}), (2, {}), (3, dict(H=2, Lq=300, Lk=300)),
+                                      (5, dict(B=3, H=2)), (4, dict(B=2, H=4, Lq=64, Lk=96))])
+def test_effective_flops_are_4d_times_oracle_pairs(cfg, over):
+    w = W.config(cfg, **over)
+    flops, _, pairs_row = bench.work(w)
+    pairs = oracle.unmasked_pairs(w.kind, w.B, w.H, w.Lq, w.Lk, w.lens, w.f64("add"))
+    assert flops == 4.0 * w.D * pairs
+    assert int(pairs_row.sum()) * w.H == pairs
+
+
+def test_llama_causal_closed_forms():
+    # 32 heads x L(L+1)/2 causal pairs; Q, K, V, O at 16 MiB each
+    w = W.config(3)
+    flops, alg, _ = bench.work(w)
+    assert flops == 4 * 128 * 32 * 2048 * 2049 // 2 == 34_376_515_584
+    assert alg == 64 * 2**20
+
+
+def test_prenorm_cross_closed_forms():
+    # no mask: B*H*Lq*Lk pairs; x, K, V, out at 128 MiB each plus gamma and beta
+    w = W.config(4)
+    flops, alg, _ = bench.work(w)
+    assert flops == 4 * 64 * 2**31
+    assert alg == 512 * 2**20 + 2 * 1024 * 2
+
+
+def test_padding_bytes_count_only_used_keys():
+    w = W.make("pad", "f16", B=2, H=3, Lq=40, Lk=50, D=16, kind=W.PADDING, seed=1,
+               lens_range=(10, 10))
+    w.lens = np.array([10, 30], np.int32)
+    _, alg, _ = bench.work(w)
+    # Q + O for every row, K + V for keys below each length, 4-byte lengths
+    assert alg == 2 * 2 * 3 * 40 * 16 * 2 + 2 * (10 + 30) * 3 * 16 * 2 + 4 * 2
+
+
+def test_multi_gpu_request_exits_with_message(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
