@@ -7,9 +7,9 @@
 //   [LNXA]  "How to fuse cross-attention and layer-norm into a single CUDA kernel?"
 //           (cms365.cn question page)
 //
-// Same method as the generic kernel -- S = scale*QK^T, mask before the
-// softmax, online softmax, O += P V with S/P in registers [MAX 2.3, 2.4;
-// MMHA 2] -- arranged for throughput on 16-bit inputs:
+// Same method as the float32 kernel (mha_kernel_f32.hpp) -- S = scale*QK^T,
+// mask before the softmax, online softmax, O += P V with S/P in registers
+// [MAX 2.3, 2.4; MMHA 2] -- arranged for throughput on 16-bit inputs:
 //   * K and V tiles go straight from HBM into LDS with buffer_load ... lds
 //     (16 bytes per lane, no register staging). Rows past Lk come back as
 //     zeros from the buffer's range check, so there are no guards or
@@ -29,7 +29,15 @@
 //     O rescale is rare; weights of up to 2^8 stay exact in fp32 and are
 //     normalised by the same running sum [MAX 2.3];
 //   * up to two workgroups per CU (launch bound: 2 waves per SIMD) so one
-//     wave's softmax overlaps another's MFMAs.
+//     wave's softmax overlaps another's MFMAs;
+//   * causal masks run two key splits per query group (8 waves), which halves
+//     the heaviest query block's serial chain; the splits' (m, l, O) states
+//     merge through LDS at the end;
+//   * bfloat16 V is rewritten once per tile into a float16 copy in LDS, so P V
+//     runs as one float16 MFMA (a tile with a value beyond the float16 range
+//     falls back to P split into two bfloat16 parts);
+//   * where P is float16, the row sum adds the packed weights the MFMA
+//     consumes (v_dot2), so numerator and normaliser see the same values.
 #pragma once
 
 #include "mha_common.hpp"

@@ -47,3 +47,13 @@ def test_padding_bytes_count_only_used_keys():
 def test_multi_gpu_request_exits_with_message(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_kernel_hash_ignores_comments_only():
+    a = 'int f(int x) { return x + 1; }  // one\n/* two */ const char* s = "// kept";'
+    b = '/* other words */\nint f(int x) {\n  return x + 1;   // three\n}\nconst char* s = "// kept";'
+    c = 'int f(int x) { return x + 2; } const char* s = "// kept";'
+    d = 'int f(int x) { return x + 1; } const char* s = "// changed";'
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    assert bench._code_only(a) != bench._code_only(d)
