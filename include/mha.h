@@ -67,7 +67,11 @@ typedef enum {
     MHA_E_MASK = 4,        /* unknown bits, PADDING with ADDITIVE, or mask NULL-ness wrong */
     MHA_E_UNSUPPORTED = 5, /* D not in {16, 32, 64, 128} */
     MHA_E_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned (lengths: 4-byte) */
-    MHA_E_OVERFLOW = 7,    /* an element count overflows int64 or the grid exceeds 2^31-1 */
+    MHA_E_OVERFLOW = 7,    /* an element count overflows int64, the grid exceeds 2^31-1, one
+                              (b, h) head's K or V reaches 4 GiB ((Lk + 256) * D * esize >
+                              2^32 - 1), or 32 rows of the additive mask do
+                              (32 * (Lk + 256) * esize > 2^32 - 1): the kernels address
+                              these through 32-bit buffer offsets */
     MHA_E_NO_DEVICE = 8,   /* no usable HIP device / runtime error while preparing */
     MHA_E_LAUNCH = 9,      /* the kernel launch itself failed */
     MHA_E_ARG = 10         /* scale or eps not finite, scale < 0, eps < 0 */

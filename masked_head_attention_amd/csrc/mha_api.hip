@@ -104,6 +104,11 @@ mha_status validate(const Call& c) {
   if (!count_ok({c.B, c.H, c.Lq, c.D}, E) || !count_ok({c.B, c.H, c.Lk, c.D}, E) ||
       !count_ok({c.B, c.Lq, c.Lk}, E))
     return MHA_E_OVERFLOW;
+  // one head's K/V, and the additive-mask rows of one wave (at most 32), are
+  // addressed through 32-bit buffer offsets, including a tile of overshoot
+  if (((int64_t)c.Lk + 256) * c.D * E > 0xFFFFFFFFLL) return MHA_E_OVERFLOW;
+  if ((c.kind & MHA_MASK_ADDITIVE) && 32 * ((int64_t)c.Lk + 256) * E > 0xFFFFFFFFLL)
+    return MHA_E_OVERFLOW;
   int bm = 0, tr = 0, tk = 0;
   if (c.dtype == MHA_F32) mha::tile_shape_f32(c.D, &bm, &tr, &tk);
   else if (c.dtype == MHA_F16) mha::tile_shape_f16(c.D, &bm, &tr, &tk);

@@ -173,15 +173,18 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
   // additive mask: 4 consecutive keys per lane and 16-key tile, one buffer per
-  // batch entry (wave-uniform); rows past Lq fall outside it. Loads are
+  // workgroup (wave-uniform); rows past Lq fall outside it. Loads are
   // 16 bytes at 4-byte alignment; entries at keys >= Lk (the next row's) are
   // replaced by -inf when used.
   __amdgpu_buffer_rsrc_t ars;
   uint32_t arow_off = 0;
   if constexpr (ADD) {
-    const char* abase = (const char*)p.add + (int64_t)b * Lq * (int64_t)Lk * E;
-    ars = make_rsrc(abase, (uint32_t)((int64_t)Lq * Lk * E));
-    arow_off = (uint32_t)qi * (uint32_t)Lk * E;
+    // based at the workgroup's first query row (64-bit arithmetic), so 32-bit
+    // offsets only span its BM rows
+    const char* abase = (const char*)p.add + ((int64_t)b * Lq + q0) * (int64_t)Lk * E;
+    const int rows = Lq - q0 > BM ? BM : Lq - q0;
+    ars = make_rsrc(abase, (uint32_t)((int64_t)rows * Lk * E));
+    arow_off = (uint32_t)(qi - q0) * (uint32_t)Lk * E;
   }
   f32x4 am_raw[2];
   // Issue order per step: mask, K, V. LDS holds chunk (c ^ swizzle(row)) of a

@@ -301,16 +301,18 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     }
   };
 
-  // additive mask: raw 16-byte groups for this lane's 2 x NB32 key runs
-  // one buffer per batch entry (wave-uniform); rows past Lq fall outside it
+  // additive mask: raw 16-byte groups for this lane's 2 x NB32 key runs.
+  // One buffer per wave, based at its first query row (64-bit arithmetic), so
+  // 32-bit offsets only span the wave's 32 rows; rows past Lq fall outside it
   const char* addrow = nullptr;
   __amdgpu_buffer_rsrc_t ars;
   uint32_t arow_off = 0;
   if constexpr (ADD) {
     const char* abase = (const char*)p.add + (int64_t)b * Lq * (int64_t)Lk * E;
     addrow = abase + (int64_t)(row_ok ? qi : 0) * Lk * E;
-    ars = make_rsrc(abase, (uint32_t)((int64_t)Lq * Lk * E));
-    arow_off = (uint32_t)qi * (uint32_t)Lk * E;
+    const int wrows = Lq - qw0 < 0 ? 0 : (Lq - qw0 > 32 ? 32 : Lq - qw0);
+    ars = make_rsrc(abase + (int64_t)qw0 * Lk * E, (uint32_t)((int64_t)wrows * Lk * E));
+    arow_off = (uint32_t)n * (uint32_t)Lk * E;
   }
   uint4 am_raw[NB32][2], am_nxt[NB32][2];
   auto load_mask = [&](int kt0, uint4 (&dst)[NB32][2]) {
