@@ -58,6 +58,7 @@ def _load():
         "oracle_prenorm_cross_fwd": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _i, _dp, _i, _i,
                                       _i, _i, _i, _d, _dp], ctypes.c_uint32),
         "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _bp], None),
+        "oracle_softmax_rows": ([_dp, _l, _i, _d, _dp], ctypes.c_uint32),
         "oracle_unmasked_pairs": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
         "oracle_tile_counts": ([_ip, _dp, _u, _i, _i, _i, _i, _i, _i, _lp], None),
         "oracle_fully_masked_rows": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
@@ -245,3 +246,17 @@ def fully_masked_rows(kind, B, H, Lq, Lk, lens=None, add=None) -> int:
     lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
     return int(_load().oracle_fully_masked_rows(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H,
                                                 Lq, Lk))
+
+
+def softmax_rows(s, scale=1.0):
+    """Row softmax of a materialised score array (last axis = one row):
+    p = exp(scale*s - max) / sum exp(scale*s - max), three passes per row
+    ["Why attention must compute the max first" 2.1]. Entries equal to -inf are
+    masked (weight 0); a row with every entry masked gives zeros and
+    FLAG_FULLY_MASKED_ROW. Returns (p, flags)."""
+    s = _f64(s)
+    cols = s.shape[-1] if s.ndim else 1
+    rows = s.size // cols if cols else 0
+    p = np.zeros(s.shape, np.float64)
+    f = _load().oracle_softmax_rows(_ptr(s, _dp), rows, cols, float(scale), _ptr(p, _dp))
+    return p, int(f)

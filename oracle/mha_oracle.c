@@ -24,6 +24,9 @@
  *                                                 naive softmax of [MAX 2.1]
  *   o_i   = sum_j p_j v_j                        [MAX 4.1 fused_attn; LNXA
  *                                                 knowledge points: S, P, O chain]
+ * Row softmax over a materialised score tensor (the standalone softmax
+ * workload of [MAX 2.1]): p_j = exp(c*s_j - max) / sum exp(c*s - max) per row,
+ * the same three passes.
  * Readings where the pages are silent or garbled (each is listed in the design
  * notes of the repository):
  *   - a row with no legal key produces o = 0 and raises FLAG_FULLY_MASKED_ROW
@@ -376,4 +379,42 @@ int64_t oracle_fully_masked_rows(const int32_t* lens, const double* add, unsigne
         }
     }
     return cnt * H;
+}
+
+/* Row softmax of a materialised score matrix [MAX 2.1: the row-softmax
+ * workload; 2.2-2.3 for what the online form must reproduce]: for each of
+ * `rows` rows of `cols` scores, p_j = exp(scale*s_j - m) / sum_k exp(scale*s_k - m)
+ * with m the row maximum, in three passes (max, normaliser, weights). An
+ * entry equal to -inf is a masked position (weight 0, whatever the scale); a
+ * row with every entry masked gets zeros and FLAG_FULLY_MASKED_ROW; a
+ * non-finite weight raises FLAG_NONFINITE. Returns the flag word. */
+uint32_t oracle_softmax_rows(const double* s, int64_t rows, int cols, double scale, double* p) {
+    uint32_t flags = 0;
+#pragma omp parallel for schedule(static) reduction(| : flags)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* x = s + r * cols;
+        double* y = p + r * cols;
+        /* pass 1: maximum of the scaled legal entries (a NaN propagates) */
+        double m = -INFINITY;
+        for (int j = 0; j < cols; ++j) {
+            if (x[j] == -INFINITY) continue;
+            double v = scale * x[j];
+            if (!(v <= m)) m = v;
+        }
+        if (m == -INFINITY) {
+            for (int j = 0; j < cols; ++j) y[j] = 0.0;
+            flags |= OR_FLAG_FULLY_MASKED_ROW;
+            continue;
+        }
+        /* pass 2: normaliser */
+        double z = 0.0;
+        for (int j = 0; j < cols; ++j)
+            if (x[j] != -INFINITY) z += exp(scale * x[j] - m);
+        /* pass 3: weights */
+        for (int j = 0; j < cols; ++j) {
+            y[j] = (x[j] == -INFINITY) ? 0.0 : exp(scale * x[j] - m) / z;
+            if (!isfinite(y[j])) flags |= OR_FLAG_NONFINITE;
+        }
+    }
+    return flags;
 }

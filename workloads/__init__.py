@@ -160,3 +160,55 @@ def config(n: int, **overrides) -> Workload:
     spec = dict(CONFIGS[n])
     spec.update(overrides)
     return make(**spec)
+
+
+# ---- the standalone row-softmax workload -----------------------------------
+@dataclasses.dataclass
+class ScoreRows:
+    """A materialised score tensor whose last axis is one softmax row."""
+    name: str
+    dtype: str
+    shape: tuple
+    scale: float
+    seed: int
+    s: Optional[np.ndarray] = None  # stored scores, `shape`
+
+    @property
+    def rows(self) -> int:
+        return int(np.prod(self.shape[:-1]))
+
+    @property
+    def cols(self) -> int:
+        return int(self.shape[-1])
+
+    def f64(self, name: str = "s") -> Optional[np.ndarray]:
+        return to_f64(getattr(self, name), self.dtype)
+
+
+def make_scores(name: str, dtype: str, shape, seed: int = 0, std: float = 2.0,
+                masked_p: float = 0.0, masked_rows: int = 0, scale: float = 1.0) -> ScoreRows:
+    """Scores ~ std * N(0, 1) rounded to ``dtype``; then, in this order, each
+    entry is set to -inf with probability ``masked_p`` and the first
+    ``masked_rows`` rows (in a random choice) entirely to -inf."""
+    rng = np.random.default_rng(seed)
+    shape = tuple(int(d) for d in shape)
+    x = _normal(rng, shape, std)
+    if masked_p > 0:
+        x = np.where(rng.random(shape) < masked_p, -np.inf, x)
+    if masked_rows > 0:
+        flat = x.reshape(-1, shape[-1])
+        pick = rng.choice(flat.shape[0], size=min(masked_rows, flat.shape[0]), replace=False)
+        flat[pick] = -np.inf
+    return ScoreRows(name=name, dtype=dtype, shape=shape, scale=scale, seed=seed,
+                     s=round_to(x, dtype))
+
+
+# the pages' row-softmax workload: a 1 x 32 x 2048 x 2048 float16 score tensor
+SOFTMAX_CONFIG = dict(name="rows-softmax-f16", dtype="f16", shape=(1, 32, 2048, 2048), seed=6,
+                      std=2.0)
+
+
+def softmax_config(**overrides) -> ScoreRows:
+    spec = dict(SOFTMAX_CONFIG)
+    spec.update(overrides)
+    return make_scores(**spec)
