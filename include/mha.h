@@ -124,6 +124,23 @@ mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, co
  * stream: launches on other streams that have not finished are not seen. */
 mha_status mha_get_flags(void* stream, uint32_t* flags, int clear);
 
+/* Row softmax of a materialised score tensor [MAX 2.1: the row-softmax
+ * workload; 2.3, 4.2: the online max/sum and the fused one-pass kernel]:
+ *   s, p  [rows, cols] in dtype, contiguous (a row = cols consecutive values)
+ *   p[r,j] = exp(scale*s[r,j] - m_r) / sum_k exp(scale*s[r,k] - m_r), with m_r
+ *   the row maximum; computed in fp32, rounded to nearest even on the store.
+ * An entry equal to -inf is a masked position: its weight is 0 whatever the
+ * scale. A row whose entries are all -inf is written as zeros and raises
+ * MHA_FLAG_FULLY_MASKED_ROW; a NaN score makes the row's unmasked weights NaN;
+ * a non-finite stored weight raises MHA_FLAG_NONFINITE (flags as mha_get_flags).
+ * scale >= 0, finite. rows or cols equal to 0 is an empty call. s and p must
+ * be aligned to the element size; 16-byte aligned rows of up to 4096
+ * (16-bit) or 2048 (float32) values take one read and one write of HBM,
+ * others two reads. p may equal s (in place); any other overlap is undefined.
+ * Asynchronous on `stream` like mha_fwd; the caller owns both tensors. */
+mha_status mha_softmax_rows(const void* s, void* p, int64_t rows, int cols, float scale,
+                            mha_dtype dtype, void* stream);
+
 /* Debug counters [MAX 6: count executions with device atomics]: a device
  * pointer to 3 uint64 values, or NULL to stop counting. While set, every
  * launch adds (tiles computed, tiles skipped, valid rows with no legal key).

@@ -120,6 +120,23 @@ def prenorm_cross_fwd(x, k, v, gamma, beta, eps: float = 1e-5, residual=None, ma
     return out
 
 
+def softmax_rows(s, out=None, scale: float = 1.0, stream=None):
+    """Row softmax over the last axis of a materialised score tensor:
+    out[..., j] = exp(scale*s[..., j] - max) / sum exp(scale*s - max); -inf
+    entries get weight 0. out may be s itself (in place)."""
+    torch = _torch()
+    _dev(s, "s")
+    cols = s.shape[-1] if s.dim() else 1
+    rows = s.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty_like(s)
+    _dev(out, "out", s.dtype, tuple(s.shape))
+    st = lib().mha_softmax_rows(_ptr(s), _ptr(out), rows, cols, float(scale), _dtype_code(s),
+                                _stream(stream))
+    check(st, "mha_softmax_rows")
+    return out
+
+
 def get_flags(clear: bool = True, stream=None) -> int:
     """Synchronise the stream and read (and by default clear) the device flag word."""
     f = ctypes.c_uint32(0)

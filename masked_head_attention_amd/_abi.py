@@ -29,6 +29,7 @@ SIGNATURES = {
     "mha_set_debug_counters": ([_vp], _i),
     "mha_tile_config": ([_i, _i, _u, ctypes.POINTER(_i), ctypes.POINTER(_i)], _i),
     "mha_status_str": ([_i], ctypes.c_char_p),
+    "mha_softmax_rows": ([_vp, _vp, ctypes.c_int64, _i, _f, _i, _vp], _i),
 }
 
 _lib = None

@@ -14,6 +14,11 @@
 
 #include "mha.h"
 #include "mha_launch.hpp"
+#include "mha_softmax.hpp"
+
+namespace mha {
+hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, bool vec_ok, hipStream_t s);
+}
 
 namespace {
 
@@ -180,6 +185,32 @@ mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, co
   Call c{nullptr, x, k, v, mask, mask_kind, gamma, beta, eps, residual,
          B, H, Lq, Lk, D, scale, dtype, stream, out, true};
   return run(c);
+}
+
+mha_status mha_softmax_rows(const void* s, void* p, int64_t rows, int cols, float scale,
+                            mha_dtype dtype, void* stream) {
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (rows < 0 || cols < 0) return MHA_E_SHAPE;
+  if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
+  if (rows == 0 || cols == 0) return MHA_OK;  // empty call
+  if (!s || !p) return MHA_E_NULL;
+  const int64_t E = elem_size(dtype);
+  if (!aligned(s, (uintptr_t)E) || !aligned(p, (uintptr_t)E)) return MHA_E_ALIGN;
+  if (!count_ok({rows, cols}, E) || (rows + 3) / 4 > 0x7fffffffLL) return MHA_E_OVERFLOW;
+  uint32_t* flags = nullptr;
+  mha_status st = device_flags(&flags);
+  if (st != MHA_OK) return st;
+  mha::SoftmaxParams sp{};
+  sp.s = s;
+  sp.p = p;
+  sp.rows = rows;
+  sp.cols = cols;
+  sp.c = scale * 1.4426950408889634f;
+  sp.flags = flags;
+  const bool vec_ok = aligned(s, 16) && aligned(p, 16) && ((int64_t)cols * E) % 16 == 0;
+  const hipError_t e =
+      mha::launch_softmax_rows(sp, (int)dtype, vec_ok, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
 }
 
 mha_status mha_get_flags(void* stream, uint32_t* flags, int clear) {

@@ -125,3 +125,27 @@ def test_tile_config_and_status_strings():
         assert lib.mha_status_str(code).decode().startswith(name)
     assert lib.mha_set_debug_counters(None) == 0
     assert lib.mha_set_debug_counters(A + 4) == _abi.STATUS_CODE["MHA_E_ALIGN"]
+
+
+def _softmax(s=A, p=A, rows=4, cols=64, scale=1.0, dtype=1):
+    return _abi.STATUS[_abi.lib().mha_softmax_rows(s, p, rows, cols, scale, dtype, None)]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), "MHA_E_DTYPE"),
+    (dict(rows=-1), "MHA_E_SHAPE"),
+    (dict(cols=-2), "MHA_E_SHAPE"),
+    (dict(scale=float("nan")), "MHA_E_ARG"),
+    (dict(scale=-1.0), "MHA_E_ARG"),
+    (dict(s=None), "MHA_E_NULL"),
+    (dict(p=None), "MHA_E_NULL"),
+    (dict(s=A + 1), "MHA_E_ALIGN"),
+    (dict(p=A + 2, dtype=0), "MHA_E_ALIGN"),
+    (dict(rows=1 << 40, cols=1 << 30), "MHA_E_OVERFLOW"),
+    (dict(rows=1 << 36, cols=1), "MHA_E_OVERFLOW"),
+    # empty calls succeed without touching a device
+    (dict(rows=0, s=None, p=None), "MHA_OK"),
+    (dict(cols=0), "MHA_OK"),
+])
+def test_softmax_validation(kw, status):
+    assert _softmax(**kw) == status
