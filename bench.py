@@ -38,6 +38,9 @@ PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}  # dense MFMA, MI355
 PEAK_HBM_GBS = 8000.0
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
 KERNEL_NAME = "mha_fwd_kernel"
+SOFTMAX_CONFIG_ID = 6
+SOFTMAX_KERNEL_NAME = "mha_softmax_rows"
+SOFTMAX_METRIC = "row softmax of a materialised score tensor: GB/s; % of HBM roofline (1 GPU)"
 
 
 # ---------------------------------------------------------------------------
@@ -114,11 +117,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_counter(workload: str, key: str = "hbm_bytes_per_launch"):
+def stored_counter(workload: str, key: str = "hbm_bytes_per_launch", kernel: str = KERNEL_NAME):
     """A per-launch figure (HBM bytes, executed MFMA FLOPs) from a committed
     rocprofv3 --pmc summary, if it was taken on the current kernel sources;
     else None."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_pmc.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -290,7 +293,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(W.CONFIGS))
+    ap.add_argument("--config", type=int, default=2,
+                    choices=sorted(W.CONFIGS) + [SOFTMAX_CONFIG_ID],
+                    help=f"workload; {SOFTMAX_CONFIG_ID} = the row softmax of a materialised "
+                         "1x32x2048x2048 float16 score tensor")
     ap.add_argument("--eager", action="store_true",
                     help="time launch-per-call steps instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -326,6 +332,9 @@ def main(argv=None):
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 6,
                           "us_per_copy": sec * 1e6, "hbm_GBs_read_plus_write": 2 * n * 4 / sec / 1e9}))
         return 0
+
+    if args.config == SOFTMAX_CONFIG_ID:
+        return main_softmax(args)
 
     import masked_head_attention_amd as M
 
@@ -378,6 +387,87 @@ def main(argv=None):
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded, workloads.py recipe)",
         "config": cfg, "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu,
         "device_flags": flags,
+        "kernel_sources_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def softmax_cpu_baseline(w, target_s: float):
+    """The fp64 oracle on a random sample of rows, repeated to ~target_s;
+    reported as algorithmic GB/s over the sample (read + write of the rows)."""
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    flat = w.s.reshape(w.rows, w.cols)
+    E = ESIZE[w.dtype]
+
+    def sample(n):
+        idx = rng.choice(w.rows, size=min(n, w.rows), replace=False)
+        return W.to_f64(flat[idx], w.dtype)
+
+    oracle.softmax_rows(sample(16), w.scale)  # warm up
+    x = sample(256)
+    t0 = time.perf_counter()
+    oracle.softmax_rows(x, w.scale)
+    per_row = (time.perf_counter() - t0) / len(x)
+    x = sample(int(min(w.rows, max(len(x), target_s / max(per_row, 1e-9)))))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.softmax_rows(x, w.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    return {"value": 2.0 * x.size * E * reps / dt / 1e9, "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{len(x)} of {w.rows} rows drawn at random (seed 1234), x{reps}; "
+                      f"{dt:.1f} s of fp64 three-pass oracle work",
+            "seconds": dt}
+
+
+def main_softmax(args):
+    """The row-softmax workload: one call = one softmax over the whole tensor."""
+    import torch
+
+    import masked_head_attention_amd as M
+
+    w = W.softmax_config()
+    E = ESIZE[w.dtype]
+    alg_bytes = 2.0 * w.rows * w.cols * E  # every score read once, every weight written once
+    s = torch.from_numpy(np.ascontiguousarray(w.s)).cuda()
+    out = torch.empty_like(s)
+    M.init()
+
+    def step():
+        M.softmax_rows(s, out=out, scale=w.scale)
+
+    M.get_flags(clear=True)
+    t_step = time_gpu(step, args.steps, args.warmup, args.eager)
+    t_eager = t_step if args.eager else time_gpu(step, min(args.steps, 100), 5, True)
+    flags = M.get_flags(clear=True)
+    achieved = alg_bytes / t_step / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": stored_counter(w.name, kernel=SOFTMAX_KERNEL_NAME)}
+    cold = None
+    if not args.no_cold:
+        t_cold = time_cold(step, args.cold_calls)
+        cold = {"us_per_call": t_cold * 1e6, "calls": args.cold_calls, "flush_mib": 512,
+                "achieved": alg_bytes / t_cold / 1e9, "unit": "GB/s",
+                "frac": alg_bytes / t_cold / 1e9 / PEAK_HBM_GBS,
+                "timing": "median of per-call HIP events, caches flushed before each call"}
+    cpu = None if args.no_cpu_baseline else softmax_cpu_baseline(w, args.cpu_seconds)
+    line = {
+        "metric": SOFTMAX_METRIC, "value": achieved, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "us_per_call": t_step * 1e6, "eager_us_per_call": t_eager * 1e6,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded, workloads.py recipe)",
+        "config": {"workload": w.name, "shape": list(w.shape), "rows": w.rows, "cols": w.cols,
+                   "scale": w.scale, "seed": w.seed, "algorithmic_bytes": alg_bytes,
+                   "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"},
+        "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu, "device_flags": flags,
         "kernel_sources_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line))
