@@ -20,7 +20,8 @@ import os
 
 import numpy as np
 
-CAUSAL, PADDING, ADDITIVE = 1, 2, 4
+CAUSAL, PADDING, ADDITIVE, KEEP, PER_HEAD = 1, 2, 4, 8, 16
+TENSOR = ADDITIVE | KEEP  # kinds that read a mask tensor
 FLAG_FULLY_MASKED_ROW, FLAG_NONFINITE, FLAG_BAD_LENGTH = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,7 +58,7 @@ def _load():
                                  _i, _i, _d, _lp, _l, _dp], ctypes.c_uint32),
         "oracle_prenorm_cross_fwd": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _i, _dp, _i, _i,
                                       _i, _i, _i, _d, _dp], ctypes.c_uint32),
-        "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _bp], None),
+        "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _i, _bp], None),
         "oracle_softmax_rows": ([_dp, _l, _i, _d, _dp], ctypes.c_uint32),
         "oracle_unmasked_pairs": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
         "oracle_tile_counts": ([_ip, _dp, _u, _i, _i, _i, _i, _i, _i, _lp], None),
@@ -84,15 +85,17 @@ def _ptr(a, typ):
     return None if a is None else a.ctypes.data_as(typ)
 
 
-def _mask_args(kind, lens, add, B, Lq, Lk):
+def _mask_args(kind, lens, add, B, Lq, Lk, H=1):
+    """Padding lengths [B]; the mask tensor (additive or keep) [B,1,Lq,Lk], or
+    [B,H,Lq,Lk] with PER_HEAD."""
     if kind & PADDING:
         lens = np.ascontiguousarray(lens, dtype=np.int32)
         if lens.shape != (B,):
             raise ValueError("lens must have shape [B]")
     else:
         lens = None
-    if kind & ADDITIVE:
-        add = _f64(add, (B, 1, Lq, Lk))
+    if kind & TENSOR:
+        add = _f64(add, (B, H if kind & PER_HEAD else 1, Lq, Lk))
     else:
         add = None
     return lens, add
@@ -113,7 +116,7 @@ def mha_fwd(q, k, v, kind=0, lens=None, add=None, scale=None):
     Lk = k.shape[2]
     k = _f64(k, (B, H, Lk, D))
     v = _f64(v, (B, H, Lk, D))
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     out = np.empty((B, H, Lq, D), np.float64)
     f = _load().oracle_mha_fwd(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip),
@@ -128,7 +131,7 @@ def mha_rows(q, k, v, rows, kind=0, lens=None, add=None, scale=None):
     Lk = k.shape[2]
     k = _f64(k, (B, H, Lk, D))
     v = _f64(v, (B, H, Lk, D))
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
     out = np.empty((rows.shape[0], D), np.float64)
@@ -144,7 +147,7 @@ def probs_row(q, k, b, h, i, kind=0, lens=None, add=None, scale=None):
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
     k = _f64(k, (B, H, Lk, D))
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     p = np.empty(Lk, np.float64)
     f = _load().oracle_probs_row(_ptr(q, _dp), _ptr(k, _dp), _ptr(lens, _ip), _ptr(add, _dp),
@@ -185,7 +188,7 @@ def _prenorm_common(x, k, v, gamma, beta, residual, kind, lens, add, scale):
     gamma = _f64(gamma, (F,))
     beta = _f64(beta, (F,))
     residual = _f64(residual, (B, Lq, F)) if residual is not None else None
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     return x, k, v, gamma, beta, residual, lens, add, scale, (B, H, Lq, Lk, D)
 
@@ -219,23 +222,24 @@ def prenorm_rows(x, k, v, gamma, beta, eps, rows, residual=None, kind=0, lens=No
     return out, int(f)
 
 
-def mask_decisions(kind, B, Lq, Lk, lens=None, add=None):
-    """uint8 [B,Lq,Lk], 1 where the pair is masked."""
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
-    dec = np.empty((B, Lq, Lk), np.uint8)
-    _load().oracle_mask_decisions(_ptr(lens, _ip), _ptr(add, _dp), kind, B, Lq, Lk,
+def mask_decisions(kind, B, Lq, Lk, lens=None, add=None, H=1):
+    """uint8 [B,Lq,Lk], 1 where the pair is masked; [B,H,Lq,Lk] with PER_HEAD."""
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
+    Hm = H if kind & PER_HEAD else 1
+    dec = np.empty((B, Hm, Lq, Lk), np.uint8)
+    _load().oracle_mask_decisions(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H, Lq, Lk,
                                   _ptr(dec, _bp))
-    return dec
+    return dec if kind & PER_HEAD else dec[:, 0]
 
 
 def unmasked_pairs(kind, B, H, Lq, Lk, lens=None, add=None) -> int:
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     return int(_load().oracle_unmasked_pairs(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H, Lq, Lk))
 
 
 def tile_counts(kind, B, H, Lq, Lk, rm, bn, lens=None, add=None):
     """(computed, skipped) tiles of rm rows x bn keys, summed over b and h."""
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     c = np.zeros(2, np.int64)
     _load().oracle_tile_counts(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H, Lq, Lk, rm, bn,
                                _ptr(c, _lp))
@@ -243,7 +247,7 @@ def tile_counts(kind, B, H, Lq, Lk, rm, bn, lens=None, add=None):
 
 
 def fully_masked_rows(kind, B, H, Lq, Lk, lens=None, add=None) -> int:
-    lens, add = _mask_args(kind, lens, add, B, Lq, Lk)
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
     return int(_load().oracle_fully_masked_rows(_ptr(lens, _ip), _ptr(add, _dp), kind, B, H,
                                                 Lq, Lk))
 

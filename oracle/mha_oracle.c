@@ -18,8 +18,10 @@
  * fusion or reordering:
  *   s_j   = scale * <q_i, k_j>                    [MAX 5.2: divide QK^T by sqrt(d_k)]
  *   mask  : an illegal position gets -inf before normalisation
- *           (causal j > i, key padding j >= len_b, or an additive mask whose
- *           -inf entries mark illegal keys)       [MMHA 1, 3.1, 4.2; MAX 2.4, 4.1]
+ *           (causal j > i, key padding j >= len_b, an additive mask whose
+ *           -inf entries mark illegal keys, or a keep-mask whose 0 entries
+ *           do; a mask tensor is shared by the heads or, PER_HEAD, one per
+ *           head)                                 [MMHA 1, 3.1, 4.2; MAX 2.4, 4.1]
  *   p_j   = exp(s_j - max) / sum exp(s - max)    three separate passes, the
  *                                                 naive softmax of [MAX 2.1]
  *   o_i   = sum_j p_j v_j                        [MAX 4.1 fused_attn; LNXA
@@ -51,7 +53,8 @@
 #include <omp.h>
 #endif
 
-enum { OR_CAUSAL = 1, OR_PADDING = 2, OR_ADDITIVE = 4 };
+enum { OR_CAUSAL = 1, OR_PADDING = 2, OR_ADDITIVE = 4, OR_KEEP = 8, OR_PER_HEAD = 16 };
+enum { OR_TENSOR = OR_ADDITIVE | OR_KEEP }; /* kinds that read a mask tensor */
 enum { OR_FLAG_FULLY_MASKED_ROW = 1, OR_FLAG_NONFINITE = 2, OR_FLAG_BAD_LENGTH = 4 };
 
 int oracle_threads(void) {
@@ -74,12 +77,26 @@ void oracle_set_threads(int n) {
  * causal: future keys (j > i) are illegal [MMHA 4.2 kernel: row < col is masked].
  * padding: keys at or beyond the sequence length are illegal [MMHA 3.1].
  * additive: an entry of -inf marks an illegal key [MMHA 1: illegal logits are
- * set to negative infinity before softmax normalisation]. */
-static int is_masked(unsigned kind, int64_t i, int64_t j, int64_t len_b, double add) {
+ * set to negative infinity before softmax normalisation].
+ * keep: an entry equal to 0 marks an illegal key, any other value keeps it
+ * [MMHA 4.2 kernel: a mask value of 0.0 becomes -inf]; keep values are never
+ * added to the logits.
+ * `m` is the mask tensor's entry for (i, j) (0 when there is none). */
+static int is_masked(unsigned kind, int64_t i, int64_t j, int64_t len_b, double m) {
     if ((kind & OR_CAUSAL) && j > i) return 1;
     if ((kind & OR_PADDING) && j >= len_b) return 1;
-    if ((kind & OR_ADDITIVE) && isinf(add) && add < 0) return 1;
+    if ((kind & OR_ADDITIVE) && isinf(m) && m < 0) return 1;
+    if ((kind & OR_KEEP) && m == 0.0) return 1;
     return 0;
+}
+
+/* Row i of the mask tensor for batch entry b and head h: [B,1,Lq,Lk], shared
+ * by the heads, or [B,H,Lq,Lk] with PER_HEAD. NULL without a mask tensor. */
+static const double* mask_row(const double* mask, unsigned kind, int64_t b, int64_t h, int H,
+                              int Lq, int Lk, int64_t i) {
+    if (!(kind & OR_TENSOR)) return NULL;
+    int64_t slab = (kind & OR_PER_HEAD) ? b * H + h : b;
+    return mask + (slab * Lq + i) * Lk;
 }
 
 static uint32_t length_flags(unsigned kind, const int32_t* lens, int B, int Lk) {
@@ -128,7 +145,7 @@ static uint32_t attention_row(const double* q, const double* K, const double* V,
     for (int j = 0; j < Lk; ++j) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d) dot += q[d] * K[(int64_t)j * D + d];
-        double add = (kind & OR_ADDITIVE) ? addrow[j] : 0.0;
+        double add = (kind & OR_TENSOR) ? addrow[j] : 0.0;
         if (is_masked(kind, i, j, len_b, add)) {
             s[j] = -INFINITY;
         } else {
@@ -177,8 +194,8 @@ uint32_t oracle_mha_fwd(const double* q, const double* k, const double* v,
         double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
 #pragma omp for schedule(dynamic, 16)
         for (int64_t r = 0; r < nrows; ++r) {
-            int64_t i = r % Lq, bh = r / Lq, b = bh / H;
-            const double* addrow = (kind & OR_ADDITIVE) ? add + ((int64_t)b * Lq + i) * Lk : NULL;
+            int64_t i = r % Lq, bh = r / Lq, b = bh / H, h = bh % H;
+            const double* addrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
             int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
             flags |= attention_row(q + r * D, k + bh * Lk * D, v + bh * Lk * D, Lk, D, scale,
                                    kind, i, len_b, addrow, s, NULL, out + r * D);
@@ -201,7 +218,7 @@ uint32_t oracle_mha_rows(const double* q, const double* k, const double* v,
         for (int64_t r = 0; r < n; ++r) {
             int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
             int64_t bh = b * H + h;
-            const double* addrow = (kind & OR_ADDITIVE) ? add + (b * Lq + i) * Lk : NULL;
+            const double* addrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
             int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
             flags |= attention_row(q + (bh * Lq + i) * D, k + bh * Lk * D, v + bh * Lk * D, Lk,
                                    D, scale, kind, i, len_b, addrow, s, NULL, out + r * D);
@@ -220,7 +237,7 @@ uint32_t oracle_probs_row(const double* q, const double* k, const int32_t* lens,
     /* V = 0 keeps the row's weights the only output of interest */
     double* vz = (double*)calloc((size_t)Lk * D + 1, sizeof(double));
     int64_t bh = (int64_t)b * H + h;
-    const double* addrow = (kind & OR_ADDITIVE) ? add + ((int64_t)b * Lq + i) * Lk : NULL;
+    const double* addrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
     int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
     uint32_t f = attention_row(q + (bh * Lq + i) * D, k + bh * Lk * D, vz, Lk, D, scale, kind,
                                i, len_b, addrow, s, p, o);
@@ -274,7 +291,7 @@ uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
             int64_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
             int64_t tok = b * Lq + i, bh = b * H + h;
             layernorm_token(x + tok * F, gamma, beta, eps, F, qfmt, y);
-            const double* addrow = (kind & OR_ADDITIVE) ? add + (b * Lq + i) * Lk : NULL;
+            const double* addrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
             int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
             double* o = out + r * D;
             flags |= attention_row(y + h * D, k + bh * Lk * D, v + bh * Lk * D, Lk, D, scale,
@@ -310,33 +327,36 @@ uint32_t oracle_prenorm_cross_fwd(const double* x, const double* k, const double
     return f;
 }
 
-/* Mask decisions as bytes: dec [B,Lq,Lk], 1 = masked. Heads share the mask. */
-void oracle_mask_decisions(const int32_t* lens, const double* add, unsigned kind, int B,
+/* Mask decisions as bytes: dec [B,Hm,Lq,Lk], 1 = masked, where Hm = H with a
+ * per-head mask tensor (PER_HEAD) and 1 otherwise (the heads share it). */
+void oracle_mask_decisions(const int32_t* lens, const double* add, unsigned kind, int B, int H,
                            int Lq, int Lk, uint8_t* dec) {
+    int Hm = (kind & OR_PER_HEAD) ? H : 1;
     for (int64_t b = 0; b < B; ++b)
-        for (int64_t i = 0; i < Lq; ++i)
-            for (int64_t j = 0; j < Lk; ++j) {
-                int64_t idx = (b * Lq + i) * Lk + j;
-                double a = (kind & OR_ADDITIVE) ? add[idx] : 0.0;
+        for (int64_t h = 0; h < Hm; ++h)
+            for (int64_t i = 0; i < Lq; ++i) {
+                const double* mrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
                 int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
-                dec[idx] = (uint8_t)is_masked(kind, i, j, len_b, a);
+                for (int64_t j = 0; j < Lk; ++j)
+                    dec[((b * Hm + h) * Lq + i) * Lk + j] =
+                        (uint8_t)is_masked(kind, i, j, len_b, mrow ? mrow[j] : 0.0);
             }
 }
 
 /* Number of legal (b, h, i, j) pairs: the work that counts as effective. */
 int64_t oracle_unmasked_pairs(const int32_t* lens, const double* add, unsigned kind, int B,
                               int H, int Lq, int Lk) {
+    int Hm = (kind & OR_PER_HEAD) ? H : 1;
     int64_t cnt = 0;
 #pragma omp parallel for reduction(+ : cnt) schedule(static)
-    for (int64_t bi = 0; bi < (int64_t)B * Lq; ++bi) {
-        int64_t b = bi / Lq, i = bi % Lq;
+    for (int64_t bhi = 0; bhi < (int64_t)B * Hm * Lq; ++bhi) {
+        int64_t i = bhi % Lq, bh = bhi / Lq, b = bh / Hm, h = bh % Hm;
         int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
-        for (int64_t j = 0; j < Lk; ++j) {
-            double a = (kind & OR_ADDITIVE) ? add[bi * Lk + j] : 0.0;
-            if (!is_masked(kind, i, j, len_b, a)) cnt++;
-        }
+        const double* mrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
+        for (int64_t j = 0; j < Lk; ++j)
+            if (!is_masked(kind, i, j, len_b, mrow ? mrow[j] : 0.0)) cnt++;
     }
-    return cnt * H;
+    return cnt * (H / Hm);
 }
 
 /* Tiles of rm query rows by bn keys (aligned at multiples of rm and bn) that
@@ -345,40 +365,46 @@ int64_t oracle_unmasked_pairs(const int32_t* lens, const double* add, unsigned k
  * the mask decisions. counts[0] = computed, counts[1] = skipped. */
 void oracle_tile_counts(const int32_t* lens, const double* add, unsigned kind, int B, int H,
                         int Lq, int Lk, int rm, int bn, int64_t* counts) {
+    int Hm = (kind & OR_PER_HEAD) ? H : 1;
     int64_t comp = 0, skip = 0;
-    for (int64_t b = 0; b < B; ++b) {
-        int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
-        for (int64_t i0 = 0; i0 < Lq; i0 += rm)
-            for (int64_t j0 = 0; j0 < Lk; j0 += bn) {
-                int legal = 0;
-                for (int64_t i = i0; i < i0 + rm && i < Lq && !legal; ++i)
-                    for (int64_t j = j0; j < j0 + bn && j < Lk; ++j) {
-                        double a = (kind & OR_ADDITIVE) ? add[(b * Lq + i) * Lk + j] : 0.0;
-                        if (!is_masked(kind, i, j, len_b, a)) { legal = 1; break; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hm; ++h) {
+            int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+            for (int64_t i0 = 0; i0 < Lq; i0 += rm)
+                for (int64_t j0 = 0; j0 < Lk; j0 += bn) {
+                    int legal = 0;
+                    for (int64_t i = i0; i < i0 + rm && i < Lq && !legal; ++i) {
+                        const double* mrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
+                        for (int64_t j = j0; j < j0 + bn && j < Lk; ++j)
+                            if (!is_masked(kind, i, j, len_b, mrow ? mrow[j] : 0.0)) {
+                                legal = 1;
+                                break;
+                            }
                     }
-                if (legal) comp++; else skip++;
-            }
-    }
-    counts[0] = comp * H;
-    counts[1] = skip * H;
+                    if (legal) comp++; else skip++;
+                }
+        }
+    counts[0] = comp * (H / Hm);
+    counts[1] = skip * (H / Hm);
 }
 
 /* Rows with no legal key, summed over b and h. */
 int64_t oracle_fully_masked_rows(const int32_t* lens, const double* add, unsigned kind, int B,
                                  int H, int Lq, int Lk) {
+    int Hm = (kind & OR_PER_HEAD) ? H : 1;
     int64_t cnt = 0;
-    for (int64_t b = 0; b < B; ++b) {
-        int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
-        for (int64_t i = 0; i < Lq; ++i) {
-            int legal = 0;
-            for (int64_t j = 0; j < Lk && !legal; ++j) {
-                double a = (kind & OR_ADDITIVE) ? add[(b * Lq + i) * Lk + j] : 0.0;
-                legal = !is_masked(kind, i, j, len_b, a);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hm; ++h) {
+            int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+            for (int64_t i = 0; i < Lq; ++i) {
+                const double* mrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
+                int legal = 0;
+                for (int64_t j = 0; j < Lk && !legal; ++j)
+                    legal = !is_masked(kind, i, j, len_b, mrow ? mrow[j] : 0.0);
+                if (!legal) cnt++;
             }
-            if (!legal) cnt++;
         }
-    }
-    return cnt * H;
+    return cnt * (H / Hm);
 }
 
 /* Row softmax of a materialised score matrix [MAX 2.1: the row-softmax

@@ -23,7 +23,7 @@ from typing import Optional
 
 import numpy as np
 
-CAUSAL, PADDING, ADDITIVE = 1, 2, 4
+CAUSAL, PADDING, ADDITIVE, KEEP, PER_HEAD = 1, 2, 4, 8, 16
 DTYPES = ("f32", "f16", "bf16")
 
 
@@ -78,7 +78,7 @@ class Workload:
     k: Optional[np.ndarray] = None  # [B,H,Lk,D]
     v: Optional[np.ndarray] = None  # [B,H,Lk,D]
     lens: Optional[np.ndarray] = None  # int32 [B] (PADDING)
-    add: Optional[np.ndarray] = None  # [B,1,Lq,Lk] stored (ADDITIVE)
+    add: Optional[np.ndarray] = None  # [B,1,Lq,Lk] ([B,H,Lq,Lk] PER_HEAD) stored (ADDITIVE, KEEP)
     prenorm: bool = False
     x: Optional[np.ndarray] = None  # [B,Lq,H*D] stored (pre-LN)
     gamma: Optional[np.ndarray] = None  # [H*D]
@@ -101,7 +101,10 @@ def make(name: str, dtype: str, B: int, H: int, Lq: int, Lk: int, D: int, kind: 
     """Draw one workload. ``lens_range`` (lo, hi) is inclusive. With ADDITIVE the
     mask holds -inf for keys >= len_b (when lens_range is given) and for each
     (b, query block, key block) of ``block`` x ``block`` chosen with probability
-    ``block_p``; diagonal blocks are never chosen; legal entries are 0."""
+    ``block_p``; diagonal blocks are never chosen; legal entries are 0. With
+    PER_HEAD the mask is [B,H,Lq,Lk], its blocks drawn per head, and legal
+    entries hold biases 0.5 * N(0, 1). KEEP draws the same pattern into a
+    keep-mask: 0 where masked, U(0.5, 2) where legal."""
     if dtype not in DTYPES:
         raise ValueError(dtype)
     rng = np.random.default_rng(seed)
@@ -119,18 +122,24 @@ def make(name: str, dtype: str, B: int, H: int, Lq: int, Lk: int, D: int, kind: 
         if lens is None:
             raise ValueError("PADDING needs lens_range")
         w.lens = lens
-    if kind & ADDITIVE:
-        add = np.zeros((B, 1, Lq, Lk), np.float64)
+    if kind & (ADDITIVE | KEEP):
+        Hm = H if kind & PER_HEAD else 1
+        masked = np.zeros((B, Hm, Lq, Lk), bool)
         if lens is not None and not (kind & PADDING):
             for b in range(B):
-                add[b, 0, :, lens[b]:] = -np.inf
+                masked[b, :, :, lens[b]:] = True
         if block_p > 0.0:
             nqb, nkb = -(-Lq // block), -(-Lk // block)
-            pick = rng.random((B, nqb, nkb)) < block_p
-            for b, qb, kb in zip(*np.nonzero(pick)):
+            pick = rng.random((B, Hm, nqb, nkb)) < block_p
+            for b, h, qb, kb in zip(*np.nonzero(pick)):
                 if qb == kb:
                     continue
-                add[b, 0, qb * block:(qb + 1) * block, kb * block:(kb + 1) * block] = -np.inf
+                masked[b, h, qb * block:(qb + 1) * block, kb * block:(kb + 1) * block] = True
+        if kind & ADDITIVE:
+            legal = _normal(rng, masked.shape, 0.5) if kind & PER_HEAD else 0.0
+            add = np.where(masked, -np.inf, legal)
+        else:
+            add = np.where(masked, 0.0, rng.uniform(0.5, 2.0, masked.shape))
         w.add = round_to(add, dtype)
     if prenorm:
         F = H * D
