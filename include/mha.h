@@ -55,16 +55,25 @@ typedef enum { MHA_F32 = 0, MHA_F16 = 1, MHA_BF16 = 2 } mha_dtype;
  *   ADDITIVE  mask points to a [B,1,Lq,Lk] tensor of dtype, shared by all
  *             heads, added to the scaled logits; an entry equal to -inf marks
  *             an illegal key (a large finite negative value is only a bias).
- * PADDING and ADDITIVE are mutually exclusive (one mask pointer); CAUSAL
- * combines with either. mask must be NULL unless PADDING or ADDITIVE is set. */
-enum { MHA_MASK_NONE = 0, MHA_MASK_CAUSAL = 1, MHA_MASK_PADDING = 2, MHA_MASK_ADDITIVE = 4 };
+ *   KEEP      mask points to a [B,1,Lq,Lk] tensor of dtype in which an entry
+ *             equal to 0 (+0 or -0) marks an illegal key and any other value
+ *             keeps it; the values are never added [MMHA 4.2 kernel: a mask
+ *             value of 0.0 becomes -inf].
+ *   PER_HEAD  with ADDITIVE or KEEP: the tensor is [B,H,Lq,Lk], one slab per
+ *             head, instead of being shared by the heads.
+ * PADDING, ADDITIVE and KEEP are mutually exclusive (one mask pointer);
+ * CAUSAL combines with any of them. mask must be NULL unless one of them is
+ * set. */
+enum { MHA_MASK_NONE = 0, MHA_MASK_CAUSAL = 1, MHA_MASK_PADDING = 2, MHA_MASK_ADDITIVE = 4,
+       MHA_MASK_KEEP = 8, MHA_MASK_PER_HEAD = 16 };
 
 typedef enum {
     MHA_OK = 0,
     MHA_E_NULL = 1,        /* a required pointer is NULL */
     MHA_E_SHAPE = 2,       /* a negative dimension, or H*D beyond the supported width */
     MHA_E_DTYPE = 3,       /* dtype is not one of mha_dtype */
-    MHA_E_MASK = 4,        /* unknown bits, PADDING with ADDITIVE, or mask NULL-ness wrong */
+    MHA_E_MASK = 4,        /* unknown bits, more than one of PADDING/ADDITIVE/KEEP, PER_HEAD
+                              without a mask tensor, or a mask given where none is used */
     MHA_E_UNSUPPORTED = 5, /* D not in {16, 32, 64, 128} */
     MHA_E_ALIGN = 6,       /* a tensor pointer is not 16-byte aligned (lengths: 4-byte) */
     MHA_E_OVERFLOW = 7,    /* an element count overflows int64, the grid exceeds 2^31-1, one

@@ -13,10 +13,11 @@ import math
 from typing import Optional
 
 from ._abi import (ADDITIVE, BF16, CAUSAL, F16, F32, FLAG_BAD_LENGTH, FLAG_FULLY_MASKED_ROW,
-                   FLAG_NONFINITE, MASK_NONE, PADDING, MhaError, check, lib)
+                   FLAG_NONFINITE, KEEP, MASK_NONE, PADDING, PER_HEAD, MhaError, check, lib)
 
-__all__ = ["fwd", "prenorm_cross_fwd", "get_flags", "set_debug_counters", "tile_config",
-           "init", "MhaError", "CAUSAL", "PADDING", "ADDITIVE", "MASK_NONE",
+__all__ = ["fwd", "prenorm_cross_fwd", "softmax_rows", "get_flags", "set_debug_counters",
+           "tile_config", "init", "MhaError", "CAUSAL", "PADDING", "ADDITIVE", "KEEP", "PER_HEAD",
+           "MASK_NONE",
            "FLAG_FULLY_MASKED_ROW", "FLAG_NONFINITE", "FLAG_BAD_LENGTH"]
 
 
@@ -58,14 +59,16 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _mask_arg(mask, kind, B, Lq, Lk, dtype):
+def _mask_arg(mask, kind, B, H, Lq, Lk, dtype):
+    """Lengths [B] (PADDING), or a mask tensor (ADDITIVE, KEEP) [B,1,Lq,Lk], or
+    [B,H,Lq,Lk] with PER_HEAD."""
     torch = _torch()
     if kind & PADDING:
         return _dev(mask, "mask (lengths)", torch.int32, (B,))
-    if kind & ADDITIVE:
-        return _dev(mask, "mask (additive)", dtype, (B, 1, Lq, Lk))
+    if kind & (ADDITIVE | KEEP):
+        return _dev(mask, "mask (tensor)", dtype, (B, H if kind & PER_HEAD else 1, Lq, Lk))
     if mask is not None:
-        raise ValueError("mask given but mask kind has neither PADDING nor ADDITIVE")
+        raise ValueError("mask given but mask kind has no PADDING, ADDITIVE or KEEP")
     return None
 
 
@@ -83,7 +86,7 @@ def fwd(q, k, v, mask=None, kind: int = MASK_NONE, scale: Optional[float] = None
     Lk = k.shape[2]
     _dev(k, "k", q.dtype, (B, H, Lk, D))
     _dev(v, "v", q.dtype, (B, H, Lk, D))
-    m = _mask_arg(mask, kind, B, Lq, Lk, q.dtype)
+    m = _mask_arg(mask, kind, B, H, Lq, Lk, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, (B, H, Lq, D))
@@ -108,7 +111,7 @@ def prenorm_cross_fwd(x, k, v, gamma, beta, eps: float = 1e-5, residual=None, ma
     _dev(gamma, "gamma", x.dtype, (F,))
     _dev(beta, "beta", x.dtype, (F,))
     _dev(residual, "residual", x.dtype, (B, Lq, F))
-    m = _mask_arg(mask, kind, B, Lq, Lk, x.dtype)
+    m = _mask_arg(mask, kind, B, H, Lq, Lk, x.dtype)
     if out is None:
         out = torch.empty_like(x)
     _dev(out, "out", x.dtype, (B, Lq, F))

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmha.so")
 
 F32, F16, BF16 = 0, 1, 2
-MASK_NONE, CAUSAL, PADDING, ADDITIVE = 0, 1, 2, 4
+MASK_NONE, CAUSAL, PADDING, ADDITIVE, KEEP, PER_HEAD = 0, 1, 2, 4, 8, 16
 FLAG_FULLY_MASKED_ROW, FLAG_NONFINITE, FLAG_BAD_LENGTH = 1, 2, 4
 STATUS = {0: "MHA_OK", 1: "MHA_E_NULL", 2: "MHA_E_SHAPE", 3: "MHA_E_DTYPE", 4: "MHA_E_MASK",
           5: "MHA_E_UNSUPPORTED", 6: "MHA_E_ALIGN", 7: "MHA_E_OVERFLOW", 8: "MHA_E_NO_DEVICE",

@@ -84,9 +84,12 @@ struct Call {
 
 mha_status validate(const Call& c) {
   if (c.dtype != MHA_F32 && c.dtype != MHA_F16 && c.dtype != MHA_BF16) return MHA_E_DTYPE;
-  if (c.kind & ~7u) return MHA_E_MASK;
-  if ((c.kind & MHA_MASK_PADDING) && (c.kind & MHA_MASK_ADDITIVE)) return MHA_E_MASK;
-  const bool wants_mask = (c.kind & (MHA_MASK_PADDING | MHA_MASK_ADDITIVE)) != 0;
+  if (c.kind & ~31u) return MHA_E_MASK;
+  const unsigned tensor = c.kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP);
+  const unsigned pointer_kinds = c.kind & (MHA_MASK_PADDING | MHA_MASK_ADDITIVE | MHA_MASK_KEEP);
+  if (pointer_kinds & (pointer_kinds - 1)) return MHA_E_MASK;  // one mask argument
+  if ((c.kind & MHA_MASK_PER_HEAD) && !tensor) return MHA_E_MASK;
+  const bool wants_mask = pointer_kinds != 0;
   if (!wants_mask && c.mask) return MHA_E_MASK;
   if (c.B < 0 || c.H < 0 || c.Lq < 0 || c.Lk < 0) return MHA_E_SHAPE;
   if (c.D != 16 && c.D != 32 && c.D != 64 && c.D != 128) return MHA_E_UNSUPPORTED;
@@ -101,18 +104,18 @@ mha_status validate(const Call& c) {
   if (c.Lk > 0 && (!c.k || !c.v)) return MHA_E_NULL;
   if (c.prenorm && (!c.gamma || !c.beta)) return MHA_E_NULL;
   const void* ptrs16[] = {c.q, c.x, c.k, c.v, c.out, c.gamma, c.beta, c.residual,
-                          (c.kind & MHA_MASK_ADDITIVE) ? c.mask : nullptr};
+                          tensor ? c.mask : nullptr};
   for (const void* p : ptrs16)
     if (p && !aligned(p, 16)) return MHA_E_ALIGN;
   if ((c.kind & MHA_MASK_PADDING) && !aligned(c.mask, 4)) return MHA_E_ALIGN;
   const int64_t E = elem_size(c.dtype);
   if (!count_ok({c.B, c.H, c.Lq, c.D}, E) || !count_ok({c.B, c.H, c.Lk, c.D}, E) ||
-      !count_ok({c.B, c.Lq, c.Lk}, E))
+      !count_ok({c.B, (c.kind & MHA_MASK_PER_HEAD) ? c.H : 1, c.Lq, c.Lk}, E))
     return MHA_E_OVERFLOW;
   // one head's K/V, and the additive-mask rows of one wave (at most 32), are
   // addressed through 32-bit buffer offsets, including a tile of overshoot
   if (((int64_t)c.Lk + 256) * c.D * E > 0xFFFFFFFFLL) return MHA_E_OVERFLOW;
-  if ((c.kind & MHA_MASK_ADDITIVE) && 32 * ((int64_t)c.Lk + 256) * E > 0xFFFFFFFFLL)
+  if (tensor && 32 * ((int64_t)c.Lk + 256) * E > 0xFFFFFFFFLL)
     return MHA_E_OVERFLOW;
   int bm = 0, tr = 0, tk = 0;
   if (c.dtype == MHA_F32) mha::tile_shape_f32(c.D, &bm, &tr, &tk);
@@ -135,7 +138,7 @@ mha_status run(const Call& c) {
   p.k = c.k;
   p.v = c.v;
   p.lens = (c.kind & MHA_MASK_PADDING) ? static_cast<const int32_t*>(c.mask) : nullptr;
-  p.add = (c.kind & MHA_MASK_ADDITIVE) ? c.mask : nullptr;
+  p.add = (c.kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP)) ? c.mask : nullptr;
   p.x = c.x;
   p.gamma = c.gamma;
   p.beta = c.beta;
@@ -145,14 +148,14 @@ mha_status run(const Call& c) {
   p.H = c.H;
   p.Lq = c.Lq;
   p.Lk = c.Lk;
-  p.kind = c.kind & (MHA_MASK_CAUSAL | MHA_MASK_PADDING);
+  p.kind = c.kind & (MHA_MASK_CAUSAL | MHA_MASK_PADDING | MHA_MASK_KEEP | MHA_MASK_PER_HEAD);
   p.c = (float)((double)c.scale * 1.4426950408889634);  // log2(e): exp(x) = 2^(x log2 e)
   p.scale = c.scale;
   p.eps = c.eps;
   p.add_vec = ((int64_t)c.Lk * elem_size(c.dtype)) % 16 == 0;
   p.flags = flags;
   p.counters = g_counters.load(std::memory_order_acquire);
-  const bool add = (c.kind & MHA_MASK_ADDITIVE) != 0;
+  const bool add = (c.kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP)) != 0;  // a mask tensor
   hipStream_t s = static_cast<hipStream_t>(c.stream);
   hipError_t e;
   if (c.dtype == MHA_F32) e = mha::launch_f32(p, c.D, add, c.prenorm, s);
@@ -239,7 +242,7 @@ mha_status mha_set_debug_counters(uint64_t* dev_counters) {
 mha_status mha_tile_config(mha_dtype dtype, int D, unsigned mask_kind, int* rows, int* keys) {
   if (!rows || !keys) return MHA_E_NULL;
   if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
-  if (mask_kind & ~7u) return MHA_E_MASK;
+  if (mask_kind & ~31u) return MHA_E_MASK;
   if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
   int bm = 0;
   if (dtype == MHA_F32) mha::tile_shape_f32(D, &bm, rows, keys);

@@ -18,7 +18,7 @@
 
 namespace mha {
 
-enum : unsigned { K_CAUSAL = 1u, K_PADDING = 2u, K_ADDITIVE = 4u };
+enum : unsigned { K_CAUSAL = 1u, K_PADDING = 2u, K_ADDITIVE = 4u, K_KEEP = 8u, K_PER_HEAD = 16u };
 enum : uint32_t { F_FULLY_MASKED_ROW = 1u, F_NONFINITE = 2u, F_BAD_LENGTH = 4u };
 
 struct Params {
@@ -35,7 +35,7 @@ struct Params {
   int B, H, Lq, Lk;
   int nqblk;             // query blocks per (b, h)
   int hg;                // heads per workgroup (pre-LN kernel of 16-bit types)
-  unsigned kind;         // K_CAUSAL | K_PADDING (ADDITIVE is a template switch)
+  unsigned kind;         // K_* bits (a mask tensor -- ADDITIVE or KEEP -- is also a template switch)
   float c;               // scale * log2(e)
   float scale;           // scale
   float eps;
@@ -152,6 +152,22 @@ __device__ inline float pair_sum(float x) {
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A keep-mask word (two 16-bit values: 0 masks the key, anything else keeps
+// it) rewritten as the additive form: a half equal to +-0 becomes `neg` (the
+// type's -inf pattern), any other half +0. Packed 16-bit integer arithmetic:
+// |x| - 1 wraps to 0xffff only for x = +-0.
+__device__ inline uint32_t keep_to_additive(uint32_t w, uint16_t neg) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  const u16x2 one = {1, 1}, n2 = {neg, neg};
+  const u16x2 zero = (u16x2)(mag - one) >> (u16x2){15, 15};
+  return __builtin_bit_cast(uint32_t, (u16x2)(zero * n2));
+}
+__device__ inline uint4 keep_to_additive(uint4 u, uint16_t neg) {
+  return make_uint4(keep_to_additive(u.x, neg), keep_to_additive(u.y, neg),
+                    keep_to_additive(u.z, neg), keep_to_additive(u.w, neg));
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory loads of this
 // wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and

@@ -181,7 +181,8 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
   if constexpr (ADD) {
     // based at the workgroup's first query row (64-bit arithmetic), so 32-bit
     // offsets only span its BM rows
-    const char* abase = (const char*)p.add + ((int64_t)b * Lq + q0) * (int64_t)Lk * E;
+    const int64_t slab = (p.kind & K_PER_HEAD) ? bh : (int64_t)b;  // shared, or per head
+    const char* abase = (const char*)p.add + (slab * Lq + q0) * (int64_t)Lk * E;
     const int rows = Lq - q0 > BM ? BM : Lq - q0;
     ars = make_rsrc(abase, (uint32_t)((int64_t)rows * Lk * E));
     arow_off = (uint32_t)(qi - q0) * (uint32_t)Lk * E;
@@ -320,7 +321,9 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kb0 + 16 * j + 4 * g + r;
-          float a = am_raw[j][r] * LOG2E;  // -inf stays -inf
+          // additive: log2 units, -inf stays -inf; keep-mask: 0 masks the key
+          float a = (p.kind & K_KEEP) ? (am_raw[j][r] == 0.f ? -INFINITY : 0.f)
+                                      : am_raw[j][r] * LOG2E;
           if (!row_ok || (edge && (key >= kpad || (causal && key > qi)))) a = -INFINITY;
           am[j][r] = a;
           any |= a != -INFINITY;

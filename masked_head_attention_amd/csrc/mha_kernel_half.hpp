@@ -308,7 +308,9 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   __amdgpu_buffer_rsrc_t ars;
   uint32_t arow_off = 0;
   if constexpr (ADD) {
-    const char* abase = (const char*)p.add + (int64_t)b * Lq * (int64_t)Lk * E;
+    // [B,1,Lq,Lk] shared by the heads, or one [Lq,Lk] slab per head
+    const int64_t slab = (p.kind & K_PER_HEAD) ? (int64_t)b * H + h : (int64_t)b;
+    const char* abase = (const char*)p.add + slab * Lq * (int64_t)Lk * E;
     addrow = abase + (int64_t)(row_ok ? qi : 0) * Lk * E;
     const int wrows = Lq - qw0 < 0 ? 0 : (Lq - qw0 > 32 ? 32 : Lq - qw0);
     ars = make_rsrc(abase + (int64_t)qw0 * Lk * E, (uint32_t)((int64_t)wrows * Lk * E));
@@ -337,6 +339,16 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           dst[blk][g] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
+  };
+
+  // a keep-mask (0 masks a key) as the additive form the tile code reads:
+  // +-0 -> -inf, anything else -> +0
+  auto to_additive = [&](uint4 (&m)[NB32][2]) {
+    constexpr uint16_t NEG = std::is_same<T, __bf16>::value ? 0xFF80 : 0xFC00;
+#pragma unroll
+    for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) m[blk][g] = keep_to_additive(m[blk][g], NEG);
   };
 
   // bf16 -> f16 rewrite of the V tile in buffer b (all key splits), same
@@ -375,7 +387,10 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 
   if (ntiles > 0) {
     issue_tile(0, 0);
-    if constexpr (ADD) load_mask(ks * BN, am_raw);
+    if constexpr (ADD) {
+      load_mask(ks * BN, am_raw);
+      if (p.kind & K_KEEP) to_additive(am_raw);
+    }
     if constexpr (CONV_V) {
       if (hl == 0 && tid < 2) vflag[tid] = -1;
     }
@@ -591,6 +606,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
         for (int g = 0; g < 2; ++g) am_raw[blk][g] = am_nxt[blk][g];
+      if (p.kind & K_KEEP) to_additive(am_raw);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's share of the next tile is in LDS
     if constexpr (CONV_V) {

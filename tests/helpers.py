@@ -72,7 +72,7 @@ def gpu_inputs(w: W.Workload):
         d[name] = to_dev(getattr(w, name), w.dtype)
     if w.kind & W.PADDING:
         d["mask"] = to_dev(w.lens, w.dtype)
-    elif w.kind & W.ADDITIVE:
+    elif w.kind & (W.ADDITIVE | W.KEEP):
         d["mask"] = to_dev(w.add, w.dtype)
     else:
         d["mask"] = None

@@ -44,7 +44,15 @@ def _pre(x=A, k=A, v=A, mask=None, kind=0, gamma=A, beta=A, eps=1e-5, residual=N
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=3), "MHA_E_DTYPE"),
-    (dict(kind=8), "MHA_E_MASK"),
+    (dict(kind=32), "MHA_E_MASK"),
+    (dict(kind=_abi.KEEP | _abi.ADDITIVE, mask=A), "MHA_E_MASK"),
+    (dict(kind=_abi.KEEP | _abi.PADDING, mask=A), "MHA_E_MASK"),
+    (dict(kind=_abi.PER_HEAD), "MHA_E_MASK"),
+    (dict(kind=_abi.PER_HEAD | _abi.PADDING, mask=A), "MHA_E_MASK"),
+    (dict(kind=_abi.KEEP, mask=None), "MHA_E_NULL"),
+    (dict(kind=_abi.KEEP, mask=A + 4), "MHA_E_ALIGN"),
+    (dict(kind=_abi.KEEP | _abi.PER_HEAD, mask=A, B=1 << 20, H=1 << 20, Lq=1 << 12, Lk=1 << 12),
+     "MHA_E_OVERFLOW"),
     (dict(kind=_abi.PADDING | _abi.ADDITIVE, mask=A), "MHA_E_MASK"),
     (dict(kind=0, mask=A), "MHA_E_MASK"),
     (dict(kind=_abi.PADDING, mask=None), "MHA_E_NULL"),
@@ -121,6 +129,7 @@ def test_tile_config_and_status_strings():
             assert (r.value, k.value) == shape
     assert lib.mha_tile_config(1, 40, 0, ctypes.byref(r), ctypes.byref(k)) == 5
     assert lib.mha_tile_config(7, 64, 0, ctypes.byref(r), ctypes.byref(k)) == 3
+    assert lib.mha_tile_config(1, 64, 32, ctypes.byref(r), ctypes.byref(k)) == 4  # E_MASK
     for code, name in _abi.STATUS.items():
         assert lib.mha_status_str(code).decode().startswith(name)
     assert lib.mha_set_debug_counters(None) == 0

@@ -108,6 +108,52 @@ def test_random_shapes(dtype, D, kind, prenorm, B, H, Lq, Lk, seed):
     _check(w, f"rand-{dtype}-D{D}-k{kind}-pre{int(prenorm)}-{B}x{H}x{Lq}x{Lk}")
 
 
+# ---- the extra mask forms: keep-masks and per-head mask tensors --------------
+KEEP, PER_HEAD = W.KEEP, W.PER_HEAD
+MASK_FORMS = [KEEP, KEEP | CAUSAL, ADDITIVE | PER_HEAD, KEEP | PER_HEAD,
+              ADDITIVE | PER_HEAD | CAUSAL]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("kind", MASK_FORMS)
+def test_mask_forms(dtype, D, kind):
+    w = W.make("mask-form", dtype, B=2, H=3, Lq=75, Lk=141, D=D, kind=kind, seed=D + kind,
+               lens_range=(1, 141), block_p=0.25, block=16)
+    _check(w, f"mask-form-{dtype}-D{D}-k{kind}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("kind", [KEEP | PER_HEAD, ADDITIVE | PER_HEAD, KEEP | CAUSAL])
+def test_prenorm_mask_forms(dtype, kind):
+    # H = 8: the 16-bit kernel serves groups of 4 heads, each with its own slab
+    w = W.make("prenorm-mask-form", dtype, B=2, H=8, Lq=70, Lk=99, D=32, kind=kind, seed=kind,
+               lens_range=(5, 99), block_p=0.2, block=16, prenorm=True, x_mean=0.5,
+               x_std=3.0, residual=True)
+    _check(w, f"prenorm-mask-form-{dtype}-k{kind}")
+
+
+def test_keep_unaligned_rows_and_counters():
+    import torch
+    import masked_head_attention_amd as M
+
+    w = W.make("keep-odd-lk", "f16", B=2, H=2, Lq=67, Lk=203, D=64, kind=KEEP | PER_HEAD | CAUSAL,
+               seed=9, lens_range=(50, 203), block_p=0.3, block=32)
+    _check(w, "keep-odd-Lk")
+    rows, keys = M.tile_config(1, w.D, w.kind)
+    cnt = torch.zeros(3, dtype=torch.int64, device="cuda")
+    M.set_debug_counters(cnt)
+    try:
+        run_gpu(w)
+        torch.cuda.synchronize()
+    finally:
+        M.set_debug_counters(None)
+    comp, skip = oracle.tile_counts(w.kind, w.B, w.H, w.Lq, w.Lk, rows, keys, w.lens,
+                                    w.f64("add"))
+    full = oracle.fully_masked_rows(w.kind, w.B, w.H, w.Lq, w.Lk, w.lens, w.f64("add"))
+    assert cnt.tolist() == [comp, skip, full], (cnt.tolist(), comp, skip, full)
+
+
 def test_unaligned_additive_rows():
     """Lk * 2 bytes not a multiple of 16: the additive mask rows are read
     element by element."""

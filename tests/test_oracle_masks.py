@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import ADDITIVE, CAUSAL, KEEP, PADDING, PER_HEAD
+from oracle import ADDITIVE, CAUSAL, KEEP, PER_HEAD
 
 
 def _qkv(rng, B, H, Lq, Lk, D):
