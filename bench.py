@@ -106,14 +106,22 @@ def _code_only(src: str) -> str:
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code (comments and layout ignored)."""
+# The sources each profiled kernel family is built from: a summary stays valid
+# while these are unchanged in code (comments and layout ignored).
+KERNEL_SOURCES = {
+    KERNEL_NAME: ("mha_common.hpp", "mha_kernel_f32.hpp", "mha_kernel_half.hpp", "mha_launch.hpp",
+                  "mha_inst_bf16.hip", "mha_inst_f16.hip", "mha_inst_f32.hip"),
+    SOFTMAX_KERNEL_NAME: ("mha_common.hpp", "mha_softmax.hpp", "mha_softmax.hip"),
+}
+
+
+def kernel_source_hash(kernel: str = KERNEL_NAME) -> str:
+    """Hash of the code (comments and layout ignored) of one kernel family's sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "masked_head_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
+    for name in sorted(KERNEL_SOURCES[kernel]):
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -128,7 +136,7 @@ def stored_counter(workload: str, key: str = "hbm_bytes_per_launch", kernel: str
         txt = f.read()
     m = re.search(r"^kernel_sources_sha256_16:\s*(\S+)", txt, re.M)
     t = re.search(r"^" + re.escape(key) + r":\s*([0-9.eE+]+)", txt, re.M)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    if not m or not t or m.group(1) != kernel_source_hash(kernel):
         return None
     return float(t.group(1))
 
@@ -468,7 +476,7 @@ def main_softmax(args):
                    "scale": w.scale, "seed": w.seed, "algorithmic_bytes": alg_bytes,
                    "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"},
         "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu, "device_flags": flags,
-        "kernel_sources_sha256_16": kernel_source_hash(),
+        "kernel_sources_sha256_16": kernel_source_hash(SOFTMAX_KERNEL_NAME),
     }
     print(json.dumps(line))
     return 0

@@ -60,6 +60,7 @@ def _load():
                                       _i, _i, _i, _d, _dp], ctypes.c_uint32),
         "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _i, _bp], None),
         "oracle_softmax_rows": ([_dp, _l, _i, _d, _dp], ctypes.c_uint32),
+        "oracle_decode": ([_dp, _dp, _dp, _ip, _i, _i, _i, _i, _d, _dp, _dp], ctypes.c_uint32),
         "oracle_unmasked_pairs": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
         "oracle_tile_counts": ([_ip, _dp, _u, _i, _i, _i, _i, _i, _i, _lp], None),
         "oracle_fully_masked_rows": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
@@ -264,3 +265,24 @@ def softmax_rows(s, scale=1.0):
     p = np.zeros(s.shape, np.float64)
     f = _load().oracle_softmax_rows(_ptr(s, _dp), rows, cols, float(scale), _ptr(p, _dp))
     return p, int(f)
+
+
+def decode(q, k, v, lens=None, scale=None):
+    """One query row per (b, h): q [B,H,D], k/v [B,H,Lk,D], optional key
+    lengths [B]. Returns (out [B,H,D], lse [B,H], flags); lse is the natural
+    log-sum-exp of the legal scaled scores (-inf for a row with none)."""
+    q = _f64(q)
+    B, H, D = q.shape
+    Lk = k.shape[2]
+    k = _f64(k, (B, H, Lk, D))
+    v = _f64(v, (B, H, Lk, D))
+    if lens is not None:
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        if lens.shape != (B,):
+            raise ValueError("lens must have shape [B]")
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((B, H, D), np.float64)
+    lse = np.empty((B, H), np.float64)
+    f = _load().oracle_decode(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip), B, H, Lk,
+                              D, scale, _ptr(out, _dp), _ptr(lse, _dp))
+    return out, lse, int(f)

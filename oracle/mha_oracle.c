@@ -29,6 +29,11 @@
  * Row softmax over a materialised score tensor (the standalone softmax
  * workload of [MAX 2.1]): p_j = exp(c*s_j - max) / sum exp(c*s - max) per row,
  * the same three passes.
+ * Decode (one new token per sequence against its key/value cache, the
+ * llama.cpp embedding of [MMHA 6.1]): the same row with Lq = 1 and per-sequence
+ * key lengths; the query is the newest position, so every cached key up to the
+ * length is legal. It also returns the row's log-sum-exp, m + log(sum exp(s -
+ * m)), the normaliser of the online softmax [MAX 2.4].
  * Readings where the pages are silent or garbled (each is listed in the design
  * notes of the repository):
  *   - a row with no legal key produces o = 0 and raises FLAG_FULLY_MASKED_ROW
@@ -441,6 +446,46 @@ uint32_t oracle_softmax_rows(const double* s, int64_t rows, int cols, double sca
             y[j] = (x[j] == -INFINITY) ? 0.0 : exp(scale * x[j] - m) / z;
             if (!isfinite(y[j])) flags |= OR_FLAG_NONFINITE;
         }
+    }
+    return flags;
+}
+
+/* Decode: one query row per (b, h) [MMHA 6.1: the llama.cpp-style call with a
+ * single new token; MAX 2.4: the fused online softmax], q [B,H,D],
+ * k/v [B,H,Lk,D], optional key lengths lens[B] (keys j >= len are illegal).
+ * out [B,H,D] = softmax-weighted sum of V; lse [B,H] = log sum_j exp(s_j) over
+ * the legal keys, in natural-log units of the scaled logits (-inf for a row
+ * with no legal key, whose output is 0 and raises FLAG_FULLY_MASKED_ROW).
+ * The same three passes as attention_row; the log-sum-exp is m + log(z). */
+uint32_t oracle_decode(const double* q, const double* k, const double* v, const int32_t* lens,
+                       int B, int H, int Lk, int D, double scale, double* out, double* lse) {
+    unsigned kind = lens ? OR_PADDING : 0;
+    uint32_t flags = length_flags(kind, lens, B, Lk);
+#pragma omp parallel reduction(| : flags)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+            int64_t b = bh / H;
+            int64_t len_b = lens ? lens[b] : Lk;
+            /* the query is the last position of its sequence: no causal test */
+            flags |= attention_row(q + bh * D, k + bh * Lk * D, v + bh * Lk * D, Lk, D, scale,
+                                   kind, 0, len_b, NULL, s, NULL, out + bh * D);
+            /* log-sum-exp of the legal scores (attention_row left them in s,
+             * -inf where masked): pass 1 max, pass 2 sum */
+            double m = -INFINITY;
+            for (int j = 0; j < Lk; ++j)
+                if (!(s[j] <= m)) m = s[j];
+            if (m == -INFINITY) {
+                lse[bh] = -INFINITY;
+                continue;
+            }
+            double z = 0.0;
+            for (int j = 0; j < Lk; ++j)
+                if (s[j] != -INFINITY) z += exp(s[j] - m);
+            lse[bh] = m + log(z);
+        }
+        free(s);
     }
     return flags;
 }

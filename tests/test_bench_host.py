@@ -57,3 +57,14 @@ def test_kernel_hash_ignores_comments_only():
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
     assert bench._code_only(a) != bench._code_only(d)
+
+
+def test_kernel_hash_per_family():
+    import os
+    csrc = os.path.join(os.path.dirname(bench.__file__), "masked_head_attention_amd", "csrc")
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        for f in files:
+            assert os.path.exists(os.path.join(csrc, f)), f
+        assert len(bench.kernel_source_hash(kernel)) == 16
+    assert bench.kernel_source_hash(bench.KERNEL_NAME) != \
+        bench.kernel_source_hash(bench.SOFTMAX_KERNEL_NAME)
