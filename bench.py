@@ -40,6 +40,8 @@ ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
 KERNEL_NAME = "mha_fwd_kernel"
 SOFTMAX_CONFIG_ID = 6
 SOFTMAX_KERNEL_NAME = "mha_softmax_rows"
+DECODE_CONFIG_ID = 7
+DECODE_KERNEL_NAME = "mha_decode"
 SOFTMAX_METRIC = "row softmax of a materialised score tensor: GB/s; % of HBM roofline (1 GPU)"
 
 
@@ -112,6 +114,7 @@ KERNEL_SOURCES = {
     KERNEL_NAME: ("mha_common.hpp", "mha_kernel_f32.hpp", "mha_kernel_half.hpp", "mha_launch.hpp",
                   "mha_inst_bf16.hip", "mha_inst_f16.hip", "mha_inst_f32.hip"),
     SOFTMAX_KERNEL_NAME: ("mha_common.hpp", "mha_softmax.hpp", "mha_softmax.hip"),
+    DECODE_KERNEL_NAME: ("mha_common.hpp", "mha_decode.hpp", "mha_decode.hip"),
 }
 
 
@@ -302,9 +305,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
-                    choices=sorted(W.CONFIGS) + [SOFTMAX_CONFIG_ID],
+                    choices=sorted(W.CONFIGS) + [SOFTMAX_CONFIG_ID, DECODE_CONFIG_ID],
                     help=f"workload; {SOFTMAX_CONFIG_ID} = the row softmax of a materialised "
-                         "1x32x2048x2048 float16 score tensor")
+                         f"1x32x2048x2048 float16 score tensor; {DECODE_CONFIG_ID} = decode, one "
+                         "new token per sequence against a float16 H=32 D=128 cache")
     ap.add_argument("--eager", action="store_true",
                     help="time launch-per-call steps instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -343,6 +347,8 @@ def main(argv=None):
 
     if args.config == SOFTMAX_CONFIG_ID:
         return main_softmax(args)
+    if args.config == DECODE_CONFIG_ID:
+        return main_decode(args)
 
     import masked_head_attention_amd as M
 
@@ -477,6 +483,100 @@ def main_softmax(args):
                    "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"},
         "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu, "device_flags": flags,
         "kernel_sources_sha256_16": kernel_source_hash(SOFTMAX_KERNEL_NAME),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def decode_work(w: W.Workload):
+    """(effective FLOPs, algorithmic bytes) of one decode call: q and out once,
+    K and V for every legal cache row, the lengths and the float32 lse."""
+    E = ESIZE[w.dtype]
+    keys = float(np.clip(w.lens, 0, w.Lk).sum()) * w.H
+    flops = 4.0 * w.D * keys
+    alg = 2.0 * w.B * w.H * w.D * E + 2.0 * keys * w.D * E + 4.0 * w.B + 4.0 * w.B * w.H
+    return flops, alg
+
+
+def decode_cpu_baseline(w: W.Workload, target_s: float):
+    """The fp64 oracle's decode on a random sample of (b, h) heads, repeated to
+    ~target_s; reported as effective TFLOP/s over the sample's legal keys."""
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    n = min(64, w.B * w.H)
+    idx = rng.choice(w.B * w.H, size=n, replace=False)
+    bs, hs = idx // w.H, idx % w.H
+    q = W.to_f64(w.q.reshape(w.B, w.H, w.D)[bs, hs][:, None], w.dtype)
+    k = W.to_f64(w.k[bs, hs][:, None], w.dtype)
+    v = W.to_f64(w.v[bs, hs][:, None], w.dtype)
+    lens = np.ascontiguousarray(w.lens[bs])
+    oracle.decode(q[:2], k[:2], v[:2], lens[:2], w.scale)  # warm up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(q, k, v, lens, w.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    flops = 4.0 * w.D * float(np.clip(lens, 0, w.Lk).sum()) * reps
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {w.B * w.H} (b,h) heads drawn at random (seed 1234), x{reps}; "
+                      f"{dt:.1f} s of fp64 three-pass oracle work",
+            "seconds": dt}
+
+
+def main_decode(args):
+    """The decode workload: one call = one new token for every sequence and
+    head (the split kernel and, when keys are split, the merge kernel)."""
+    import torch
+
+    import masked_head_attention_amd as M
+
+    w = W.decode_config()
+    flops, alg_bytes = decode_work(w)
+    d = gpu_setup(w)
+    q = d["q"].view(w.B, w.H, w.D)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    code = {"f32": M.F32, "f16": M.F16, "bf16": M.BF16}[w.dtype]
+    ws = torch.empty(max(1, M.decode_workspace_size(w.B, w.H, w.Lk, w.D, code)),
+                     dtype=torch.uint8, device="cuda")
+    M.init()
+
+    def step():
+        M.decode(q, d["k"], d["v"], d["mask"], scale=w.scale, out=out, lse=lse, workspace=ws)
+
+    M.get_flags(clear=True)
+    t_step = time_gpu(step, args.steps, args.warmup, args.eager)
+    t_eager = t_step if args.eager else time_gpu(step, min(args.steps, 100), 5, True)
+    flags = M.get_flags(clear=True)
+    achieved = alg_bytes / t_step / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": stored_counter(w.name, kernel=DECODE_KERNEL_NAME),
+            "timed": "whole call (split kernel + merge kernel)"}
+    cold = None
+    if not args.no_cold:
+        t_cold = time_cold(step, args.cold_calls)
+        cold = {"us_per_call": t_cold * 1e6, "calls": args.cold_calls, "flush_mib": 512,
+                "achieved": alg_bytes / t_cold / 1e9, "unit": "GB/s",
+                "frac": alg_bytes / t_cold / 1e9 / PEAK_HBM_GBS,
+                "timing": "median of per-call HIP events, caches flushed before each call"}
+    cpu = None if args.no_cpu_baseline else decode_cpu_baseline(w, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": flops / t_step / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "us_per_call": t_step * 1e6, "eager_us_per_call": t_eager * 1e6,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded, workloads.py recipe)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": 1, "Lk": w.Lk, "D": w.D,
+                   "mask": "cache lengths", "seed": w.seed, "effective_flops": flops,
+                   "algorithmic_bytes": alg_bytes,
+                   "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"},
+        "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu, "device_flags": flags,
+        "kernel_sources_sha256_16": kernel_source_hash(DECODE_KERNEL_NAME),
     }
     print(json.dumps(line))
     return 0

@@ -9,7 +9,8 @@
  *   [LNXA]  "How to fuse cross-attention and layer-norm into a single CUDA
  *           kernel?" (cms365.cn question page)
  *
- * One call is one kernel launch on the caller's stream. Inside it, for every
+ * One call is one kernel launch on the caller's stream (decode: at most two,
+ * see mha_decode_fwd). Inside it, for every
  * (batch, head, query) row: S = scale * Q K^T, a causal / key-padding /
  * additive mask applied before normalisation, a numerically stable online
  * softmax (running row max, rescaled running sum), and P V accumulated in
@@ -36,6 +37,7 @@
 #ifndef MHA_H
 #define MHA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -83,7 +85,9 @@ typedef enum {
                               these through 32-bit buffer offsets */
     MHA_E_NO_DEVICE = 8,   /* no usable HIP device / runtime error while preparing */
     MHA_E_LAUNCH = 9,      /* the kernel launch itself failed */
-    MHA_E_ARG = 10         /* scale or eps not finite, scale < 0, eps < 0 */
+    MHA_E_ARG = 10,        /* scale or eps not finite, scale < 0, eps < 0 */
+    MHA_E_WORKSPACE = 11   /* the decode workspace is NULL, not 16-byte aligned or smaller
+                              than mha_decode_workspace_size reports */
 } mha_status;
 
 /* Device flag word bits (ORed by kernels, cleared by mha_get_flags). */
@@ -149,6 +153,42 @@ mha_status mha_get_flags(void* stream, uint32_t* flags, int clear);
  * Asynchronous on `stream` like mha_fwd; the caller owns both tensors. */
 mha_status mha_softmax_rows(const void* s, void* p, int64_t rows, int cols, float scale,
                             mha_dtype dtype, void* stream);
+
+/* Decode: one new query row per (batch, head) against a key/value cache
+ * [MMHA 6.1: the kernel called from an inference engine's cache update with
+ * one new token per sequence; MAX 2.3-2.4: the online softmax, whose running
+ * (maximum, sum, output) states of disjoint key ranges merge exactly].
+ *   q     [B,H,D]      the new token's queries
+ *   k, v  [B,H,Lk,D]   the caches; Lk is their capacity
+ *   lens  int32 [B] in device memory, or NULL: keys j >= lens[b] are illegal
+ *         for sequence b (the padding mask of mha_fwd with Lq = 1). A length
+ *         outside [0, Lk] acts clamped and raises MHA_FLAG_BAD_LENGTH.
+ *   out   [B,H,D]      o[b,h,:] = sum_j softmax_j(scale * q.k_j) v_j over the
+ *                      legal keys; 0 (and MHA_FLAG_FULLY_MASKED_ROW) for a
+ *                      sequence with no legal key.
+ *   lse   float32 [B,H] or NULL: log(sum_j exp(scale * q.k_j)) over the legal
+ *         keys (natural log; -inf for a row with no legal key). It is the
+ *         normaliser that merges this result with attention over other keys.
+ *   workspace, workspace_bytes: device scratch for the per-split partial
+ *         results, at least mha_decode_workspace_size(...) bytes, 16-byte
+ *         aligned, owned by the caller; NULL is allowed when that size is 0.
+ *         Its contents need no initialisation and are meaningless afterwards.
+ *         Calls that overlap in time must not share a workspace.
+ * The keys of a head are split into chunks processed by separate waves when
+ * that fills the GPU better; then a second, small kernel merges the chunks
+ * (two launches on `stream`), otherwise one launch writes the result.
+ * Validation, errors and flags as mha_fwd; B or H equal to 0 is an empty
+ * call; Lk may be 0 (every row fully masked). */
+mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int32_t* lens,
+                          int B, int H, int Lk, int D, float scale, mha_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream, void* out,
+                          float* lse);
+
+/* Workspace bytes mha_decode_fwd needs for these sizes (0 when every head is
+ * one split). Pure host computation: no device is touched. Fails with the
+ * same shape/dtype status codes as mha_decode_fwd. */
+mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
+                                     size_t* bytes);
 
 /* Debug counters [MAX 6: count executions with device atomics]: a device
  * pointer to 3 uint64 values, or NULL to stop counting. While set, every

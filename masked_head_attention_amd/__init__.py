@@ -15,7 +15,8 @@ from typing import Optional
 from ._abi import (ADDITIVE, BF16, CAUSAL, F16, F32, FLAG_BAD_LENGTH, FLAG_FULLY_MASKED_ROW,
                    FLAG_NONFINITE, KEEP, MASK_NONE, PADDING, PER_HEAD, MhaError, check, lib)
 
-__all__ = ["fwd", "prenorm_cross_fwd", "softmax_rows", "get_flags", "set_debug_counters",
+__all__ = ["fwd", "prenorm_cross_fwd", "softmax_rows", "decode", "decode_workspace_size",
+           "get_flags", "set_debug_counters",
            "tile_config", "init", "MhaError", "CAUSAL", "PADDING", "ADDITIVE", "KEEP", "PER_HEAD",
            "MASK_NONE",
            "FLAG_FULLY_MASKED_ROW", "FLAG_NONFINITE", "FLAG_BAD_LENGTH"]
@@ -138,6 +139,48 @@ def softmax_rows(s, out=None, scale: float = 1.0, stream=None):
                                 _stream(stream))
     check(st, "mha_softmax_rows")
     return out
+
+
+def decode_workspace_size(B: int, H: int, Lk: int, D: int, dtype_code: int) -> int:
+    """Bytes of device workspace that decode needs for these sizes (0 if none)."""
+    n = ctypes.c_size_t(0)
+    check(lib().mha_decode_workspace_size(B, H, Lk, D, dtype_code, ctypes.byref(n)),
+          "mha_decode_workspace_size")
+    return int(n.value)
+
+
+def decode(q, k, v, lens=None, scale: Optional[float] = None, out=None, lse=None,
+           with_lse: bool = True, workspace=None, stream=None):
+    """One new query row per (b, h) against a key/value cache.
+    q [B,H,D], k/v [B,H,Lk,D], lens int32 [B] or None -> (out [B,H,D], lse
+    float32 [B,H] or None). ``workspace`` is a uint8 GPU tensor of at least
+    decode_workspace_size(...) bytes; when omitted one is allocated here."""
+    torch = _torch()
+    _dev(q, "q")
+    B, H, D = q.shape
+    Lk = k.shape[2]
+    _dev(k, "k", q.dtype, (B, H, Lk, D))
+    _dev(v, "v", q.dtype, (B, H, Lk, D))
+    _dev(lens, "lens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, (B, H, D))
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", torch.float32, (B, H))
+    code = _dtype_code(q)
+    need = decode_workspace_size(B, H, Lk, D, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().mha_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(lens), B, H, Lk, D, scale, code,
+                              _ptr(workspace), ws_bytes, _stream(stream), _ptr(out), _ptr(lse))
+    check(st, "mha_decode_fwd")
+    return out, lse
 
 
 def get_flags(clear: bool = True, stream=None) -> int:

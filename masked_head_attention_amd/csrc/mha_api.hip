@@ -14,10 +14,13 @@
 
 #include "mha.h"
 #include "mha_launch.hpp"
+#include "mha_decode.hpp"
 #include "mha_softmax.hpp"
 
 namespace mha {
 hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, bool vec_ok, hipStream_t s);
+void decode_plan(int B, int H, int Lk, int D, int esize, int* chunk, int* nsplit);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t s);
 }
 
 namespace {
@@ -164,9 +167,79 @@ mha_status run(const Call& c) {
   return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
 }
 
+// Decode: shape checks shared by the workspace query and the call. On success
+// *chunk, *nsplit hold the split plan and *ws the workspace bytes it needs.
+mha_status decode_check(int B, int H, int Lk, int D, mha_dtype dtype, int* chunk, int* nsplit,
+                        size_t* ws) {
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (B < 0 || H < 0 || Lk < 0) return MHA_E_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
+  const int64_t E = elem_size(dtype);
+  if (!count_ok({B, H, Lk, D}, E)) return MHA_E_OVERFLOW;
+  if (((int64_t)Lk + 256) * D * E > 0xFFFFFFFFLL) return MHA_E_OVERFLOW;
+  mha::decode_plan(B, H, Lk, D, (int)E, chunk, nsplit);
+  const int64_t waves = (int64_t)B * H * *nsplit;
+  if (waves > 0x7fffffffLL) return MHA_E_OVERFLOW;
+  *ws = *nsplit > 1 ? (size_t)waves * (size_t)(D + 2) * sizeof(float) : 0;
+  return MHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
+                                     size_t* bytes) {
+  if (!bytes) return MHA_E_NULL;
+  int chunk = 0, nsplit = 0;
+  size_t ws = 0;
+  mha_status st = decode_check(B, H, Lk, D, dtype, &chunk, &nsplit, &ws);
+  if (st != MHA_OK) return st;
+  *bytes = ws;
+  return MHA_OK;
+}
+
+mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int32_t* lens,
+                          int B, int H, int Lk, int D, float scale, mha_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream, void* out,
+                          float* lse) {
+  int chunk = 0, nsplit = 0;
+  size_t ws = 0;
+  mha_status st = decode_check(B, H, Lk, D, dtype, &chunk, &nsplit, &ws);
+  if (st != MHA_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
+  if (B == 0 || H == 0) return MHA_OK;  // empty call
+  if (!q || !out) return MHA_E_NULL;
+  if (Lk > 0 && (!k || !v)) return MHA_E_NULL;
+  const void* ptrs16[] = {q, k, v, out};
+  for (const void* p : ptrs16)
+    if (p && !aligned(p, 16)) return MHA_E_ALIGN;
+  if ((lens && !aligned(lens, 4)) || (lse && !aligned(lse, 4))) return MHA_E_ALIGN;
+  if (ws > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < ws))
+    return MHA_E_WORKSPACE;
+  uint32_t* flags = nullptr;
+  st = device_flags(&flags);
+  if (st != MHA_OK) return st;
+  mha::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.lens = lens;
+  p.out = out;
+  p.lse = lse;
+  const int64_t slots = (int64_t)B * H * nsplit;
+  p.part_o = ws > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.part_ml = ws > 0 ? static_cast<float*>(workspace) + slots * D : nullptr;
+  p.B = B;
+  p.H = H;
+  p.Lk = Lk;
+  p.chunk = chunk;
+  p.nsplit = nsplit;
+  p.c = (float)((double)scale * 1.4426950408889634);  // log2(e): exp(x) = 2^(x log2 e)
+  p.flags = flags;
+  const hipError_t e = mha::launch_decode(p, (int)dtype, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
+}
 
 mha_status mha_init(void) {
   uint32_t* f = nullptr;
@@ -264,6 +337,7 @@ const char* mha_status_str(mha_status s) {
     case MHA_E_NO_DEVICE: return "MHA_E_NO_DEVICE: no usable HIP device";
     case MHA_E_LAUNCH: return "MHA_E_LAUNCH: kernel launch failed";
     case MHA_E_ARG: return "MHA_E_ARG: scale or eps out of range";
+    case MHA_E_WORKSPACE: return "MHA_E_WORKSPACE: workspace missing, misaligned or too small";
   }
   return "unknown mha_status";
 }

@@ -158,3 +158,57 @@ def _softmax(s=A, p=A, rows=4, cols=64, scale=1.0, dtype=1):
 ])
 def test_softmax_validation(kw, status):
     assert _softmax(**kw) == status
+
+
+def _dec(q=A, k=A, v=A, lens=None, B=2, H=4, Lk=4096, D=128, scale=0.125, dtype=1, ws=A,
+         ws_bytes=1 << 30, out=A, lse=None):
+    return _abi.STATUS[_abi.lib().mha_decode_fwd(q, k, v, lens, B, H, Lk, D, scale, dtype, ws,
+                                                 ws_bytes, None, out, lse)]
+
+
+def _ws(B, H, Lk, D, dtype=1):
+    n = ctypes.c_size_t(0)
+    st = _abi.STATUS[_abi.lib().mha_decode_workspace_size(B, H, Lk, D, dtype, ctypes.byref(n))]
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), "MHA_E_DTYPE"),
+    (dict(B=-1), "MHA_E_SHAPE"),
+    (dict(Lk=-1), "MHA_E_SHAPE"),
+    (dict(D=96), "MHA_E_UNSUPPORTED"),
+    (dict(scale=float("nan")), "MHA_E_ARG"),
+    (dict(scale=-1.0), "MHA_E_ARG"),
+    (dict(q=None), "MHA_E_NULL"),
+    (dict(out=None), "MHA_E_NULL"),
+    (dict(v=None), "MHA_E_NULL"),
+    (dict(k=A + 8), "MHA_E_ALIGN"),
+    (dict(lens=A + 2), "MHA_E_ALIGN"),
+    (dict(lse=A + 1), "MHA_E_ALIGN"),
+    (dict(ws=None), "MHA_E_WORKSPACE"),
+    (dict(ws=A + 4), "MHA_E_WORKSPACE"),
+    (dict(ws_bytes=16), "MHA_E_WORKSPACE"),
+    (dict(B=1, H=1, Lk=1 << 24, D=128), "MHA_E_OVERFLOW"),
+    # empty calls succeed without touching a device
+    (dict(B=0), "MHA_OK"),
+    (dict(H=0, q=None, out=None), "MHA_OK"),
+])
+def test_decode_validation(kw, status):
+    assert _dec(**kw) == status
+
+
+def test_decode_workspace_size():
+    # one split per head when the cache is short: no workspace
+    assert _ws(2, 4, 37, 128) == ("MHA_OK", 0)
+    assert _ws(0, 4, 4096, 128) == ("MHA_OK", 0)
+    # split keys: B*H*nsplit partial rows of D floats plus (m, l)
+    st, n = _ws(16, 32, 4096, 128)
+    assert st == "MHA_OK" and n > 0 and n % (16 * 32 * 130 * 4) == 0
+    nsplit = n // (16 * 32 * 130 * 4)
+    assert nsplit > 1 and 4096 % nsplit == 0
+    # fewer heads: more splits per head to fill the GPU, never below 64-key chunks
+    st, n1 = _ws(1, 2, 4096, 128)
+    assert st == "MHA_OK" and n1 // (2 * 130 * 4) == 4096 // 64
+    assert _ws(1, 1, 10, 48)[0] == "MHA_E_UNSUPPORTED"
+    assert _ws(1, 1, 10, 64, dtype=9)[0] == "MHA_E_DTYPE"
+    assert _ws(1, -1, 10, 64)[0] == "MHA_E_SHAPE"

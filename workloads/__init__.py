@@ -221,3 +221,21 @@ def softmax_config(**overrides) -> ScoreRows:
     spec = dict(SOFTMAX_CONFIG)
     spec.update(overrides)
     return make_scores(**spec)
+
+
+# ---- the decode workload -----------------------------------------------------
+# One new token per sequence against a Llama-2-7B-shaped key/value cache
+# (H=32, D=128, float16) of capacity 4096, per-sequence cache lengths uniform
+# in [256, 4096]; q, k, v = 0.5 * N(0, 1) as in the causal Llama-2 workload.
+# Drawn by `make` with Lq = 1 (q [B,H,1,D] is the decode layout [B,H,D]) and
+# the padding lengths as the cache lengths.
+DECODE_CONFIG = dict(name="llama2-7b-decode-f16", dtype="f16", B=16, H=32, Lq=1, Lk=4096, D=128,
+                     kind=PADDING, lens_range=(256, 4096), qkv_std=0.5, seed=7)
+
+
+def decode_config(**overrides) -> Workload:
+    spec = dict(DECODE_CONFIG)
+    spec.update(overrides)
+    if spec.get("Lq", 1) != 1:
+        raise ValueError("decode has one query row")
+    return make(**spec)
