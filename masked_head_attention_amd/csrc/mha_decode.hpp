@@ -165,7 +165,10 @@ __device__ inline int decode_len(const DecodeParams& p, int b, bool* bad) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
+// Four waves per SIMD: registers for two K/V buffers per wave, which keeps
+// the compiler from trading the prefetch for occupancy.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+decode_split_kernel(const DecodeParams p) {
   using C = DecCfg<T, D>;
   constexpr int EPL = C::EPL, U = C::U, G = C::G, LPK = C::LPK, RB = C::RB;
   const int lane = threadIdx.x & 63;
@@ -174,9 +177,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   const uint32_t wid =
       blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (wid >= (uint32_t)(p.B * p.H * p.nsplit)) return;  // whole waves only
-  const uint32_t bh32 = wid / (uint32_t)p.nsplit;
+  // the split index is the slow one: consecutive workgroups take the same
+  // split of neighbouring heads, so the CUs that the round-robin placement
+  // feeds each receive a mix of early (always legal) and late splits
+  const uint32_t nbh = (uint32_t)(p.B * p.H);
+  const int s = (int)(wid / nbh);
+  const uint32_t bh32 = wid - (uint32_t)s * nbh;
   const int64_t bh = bh32;
-  const int s = (int)(wid - bh32 * (uint32_t)p.nsplit);
   bool bad = false;
   const int len = decode_len(p, (int)(bh32 / (uint32_t)p.H), &bad);
   const int start = s * p.chunk;
@@ -187,8 +194,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 
   const char* kh = static_cast<const char*>(p.k) + bh * (int64_t)p.Lk * RB;
   const char* vh = static_cast<const char*>(p.v) + bh * (int64_t)p.Lk * RB;
-  const auto krs = make_rsrc(kh, (uint32_t)len * RB);  // rows >= len read as zeros
-  const auto vrs = make_rsrc(vh, (uint32_t)len * RB);
+  // rows at or past the split's end read as zeros and move no data, so the
+  // prefetch of the iteration after the last one is free
+  const auto krs = make_rsrc(kh, (uint32_t)end * RB);
+  const auto vrs = make_rsrc(vh, (uint32_t)end * RB);
   const uint4 qv =
       *reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) + bh * RB + sub * 16);
   T* tag = nullptr;
@@ -197,8 +206,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 #pragma unroll
   for (int f = 0; f < EPL; ++f) o[f] = 0.f;
 
-  for (int kb = start; kb < end; kb += C::KPI) {
-    uint4 kr[U], vr[U];
+  auto issue = [&](int kb, uint4 (&kr)[U], uint4 (&vr)[U]) {
     const uint32_t off0 = (uint32_t)(kb + g) * RB + sub * 16;
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -208,6 +216,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     for (int u = 0; u < U; ++u)
       vr[u] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off0 + u * G * RB, 0, 0));
+  };
+  auto consume = [&](int kb, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
     float t[U];
     float mx = m;
 #pragma unroll
@@ -231,6 +241,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
       for (int f = 0; f < EPL; ++f) o[f] = __builtin_fmaf(pu, vf[f], o[f]);
     }
     m = mx;
+  };
+
+  // two register buffers: the next iteration's loads are in flight while the
+  // current one is consumed
+  uint4 ka[U], va[U], kb2[U], vb2[U];
+  if (start < end) issue(start, ka, va);
+  for (int kb = start; kb < end; kb += 2 * C::KPI) {
+    issue(kb + C::KPI, kb2, vb2);
+    consume(kb, ka, va);
+    if (kb + C::KPI >= end) break;
+    issue(kb + 2 * C::KPI, ka, va);
+    consume(kb + C::KPI, kb2, vb2);
   }
 
   // merge the G key groups of the wave (log-sum-exp), lanes with equal `sub`
@@ -294,21 +316,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const int ns = (len + p.chunk - 1) / p.chunk;  // splits holding a legal key
   const float* ml = p.part_ml + bh * p.nsplit * 2;
   const float* po = p.part_o + bh * p.nsplit * D;
+  // split s's (m, l) is read by lane s % 64; maxima and sums are wave reductions
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
   const float Mu = (M == -INFINITY) ? 0.f : M;
   float L = 0.f, O[FPL];
 #pragma unroll
   for (int r = 0; r < FPL; ++r) O[r] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2_fast(ml[2 * s] - Mu);
-    L = __builtin_fmaf(ml[2 * s + 1], w, L);
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float2 mls = s < ns ? *reinterpret_cast<const float2*>(ml + 2 * s) : make_float2(0.f, 0.f);
+    const float w = s < ns ? exp2_fast(mls.x - Mu) : 0.f;  // weight of split s
+    L = __builtin_fmaf(mls.y, w, L);
+    const int n = min(64, ns - s0);
+    // the partial outputs of this group of splits: independent loads
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) {
+      const float wj = __shfl(w, j, 64);
 #pragma unroll
-    for (int r = 0; r < FPL; ++r) {
-      const int f = lane + 64 * r;
-      if (f < D) O[r] = __builtin_fmaf(po[(int64_t)s * D + f], w, O[r]);
+      for (int r = 0; r < FPL; ++r) {
+        const int f = lane + 64 * r;
+        if (f < D) O[r] = __builtin_fmaf(po[(int64_t)(s0 + j) * D + f], wj, O[r]);
+      }
     }
   }
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) L += __shfl_xor(L, x, 64);
   const float inv = (L == 0.f) ? 0.f : 1.0f / L;
   bool nonfinite = false;
   T* out = static_cast<T*>(p.out) + bh * D;
