@@ -325,20 +325,31 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   float L = 0.f, O[FPL];
 #pragma unroll
   for (int r = 0; r < FPL; ++r) O[r] = 0.f;
+  constexpr int SB = 8;  // splits whose partial outputs are loaded together
   for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    const float2 mls = s < ns ? *reinterpret_cast<const float2*>(ml + 2 * s) : make_float2(0.f, 0.f);
-    const float w = s < ns ? exp2_fast(mls.x - Mu) : 0.f;  // weight of split s
-    L = __builtin_fmaf(mls.y, w, L);
     const int n = min(64, ns - s0);
-    // the partial outputs of this group of splits: independent loads
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) {
-      const float wj = __shfl(w, j, 64);
+    float w = 0.f;  // weight of split s0 + lane
+    if (lane < n) {
+      const float2 v = *reinterpret_cast<const float2*>(ml + 2 * (s0 + lane));
+      w = exp2_fast(v.x - Mu);
+      L = __builtin_fmaf(v.y, w, L);
+    }
+    for (int j0 = 0; j0 < n; j0 += SB) {
+      float x[SB][FPL];
 #pragma unroll
-      for (int r = 0; r < FPL; ++r) {
-        const int f = lane + 64 * r;
-        if (f < D) O[r] = __builtin_fmaf(po[(int64_t)(s0 + j) * D + f], wj, O[r]);
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int r = 0; r < FPL; ++r) {
+          const int f = lane + 64 * r;
+          x[j][r] = (j0 + j < n && f < D) ? po[(int64_t)(s0 + j0 + j) * D + f] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const float wj =
+            (j0 + j < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j0 + j))
+                         : 0.f;
+#pragma unroll
+        for (int r = 0; r < FPL; ++r) O[r] = __builtin_fmaf(x[j][r], wj, O[r]);
       }
     }
   }
