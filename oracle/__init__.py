@@ -1,4 +1,5 @@
-"""Plain fp64 CPU reference for the masked multi-head attention forward.
+"""Plain fp64 CPU reference for the masked multi-head attention forward (and
+its backward, decode and row-softmax variants).
 
 TEST INFRASTRUCTURE ONLY: the test-suite, the package smoke check and the
 CPU-baseline leg of the benchmark are the only callers. The GPU library never
@@ -61,6 +62,8 @@ def _load():
         "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _i, _bp], None),
         "oracle_softmax_rows": ([_dp, _l, _i, _d, _dp], ctypes.c_uint32),
         "oracle_decode": ([_dp, _dp, _dp, _ip, _i, _i, _i, _i, _d, _dp, _dp], ctypes.c_uint32),
+        "oracle_mha_bwd": ([_dp, _dp, _dp, _dp, _ip, _dp, _u, _i, _i, _i, _i, _i, _d, _dp, _dp,
+                            _dp], ctypes.c_uint32),
         "oracle_unmasked_pairs": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
         "oracle_tile_counts": ([_ip, _dp, _u, _i, _i, _i, _i, _i, _i, _lp], None),
         "oracle_fully_masked_rows": ([_ip, _dp, _u, _i, _i, _i, _i], _l),
@@ -286,3 +289,24 @@ def decode(q, k, v, lens=None, scale=None):
     f = _load().oracle_decode(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip), B, H, Lk,
                               D, scale, _ptr(out, _dp), _ptr(lse, _dp))
     return out, lse, int(f)
+
+
+def mha_bwd(q, k, v, dout, kind=0, lens=None, add=None, scale=None):
+    """Gradients of mha_fwd for the upstream gradient dout [B,H,Lq,D]
+    ("Why attention must compute the max first" 3.3: the softmax Jacobian).
+    Returns (dq [B,H,Lq,D], dk, dv [B,H,Lk,D], flags)."""
+    q = _f64(q)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    k = _f64(k, (B, H, Lk, D))
+    v = _f64(v, (B, H, Lk, D))
+    dout = _f64(dout, (B, H, Lq, D))
+    lens, add = _mask_args(kind, lens, add, B, Lq, Lk, H)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    f = _load().oracle_mha_bwd(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(dout, _dp),
+                               _ptr(lens, _ip), _ptr(add, _dp), int(kind), B, H, Lq, Lk, D, scale,
+                               _ptr(dq, _dp), _ptr(dk, _dp), _ptr(dv, _dp))
+    return dq, dk, dv, int(f)

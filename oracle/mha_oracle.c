@@ -34,6 +34,10 @@
  * key lengths; the query is the newest position, so every cached key up to the
  * length is legal. It also returns the row's log-sum-exp, m + log(sum exp(s -
  * m)), the normaliser of the online softmax [MAX 2.4].
+ * Backward (the gradients of the forward for an upstream gradient dO): the
+ * softmax Jacobian dp_j/ds_k = p_j (delta_jk - p_k) of [MAX 3.3], chained
+ * through S = scale * Q K^T and O = P V; the row maximum carries no gradient
+ * (the weights do not depend on it, [MAX 3.3]).
  * Readings where the pages are silent or garbled (each is listed in the design
  * notes of the repository):
  *   - a row with no legal key produces o = 0 and raises FLAG_FULLY_MASKED_ROW
@@ -486,6 +490,73 @@ uint32_t oracle_decode(const double* q, const double* k, const double* v, const 
             lse[bh] = m + log(z);
         }
         free(s);
+    }
+    return flags;
+}
+
+/* Backward of oracle_mha_fwd for an upstream gradient dout = dL/dO
+ * [MAX 3.3: the softmax Jacobian dp_j/ds_k = p_j (delta_jk - p_k)]. Per row i
+ * of head (b, h), with p the forward's weights (the same three passes, 0 at
+ * masked keys):
+ *   dV_j  += p_ij dO_i
+ *   dP_ij  = <dO_i, v_j>
+ *   dS_ij  = sum_k dP_ik dp_ik/ds_ij = p_ij (dP_ij - sum_k p_ik dP_ik)
+ *   dQ_i   = scale sum_j dS_ij k_j,   dK_j += scale dS_ij q_i
+ * Masked keys are skipped (they have no weight and no gradient); a fully
+ * masked row contributes nothing and has dQ = 0. The additive mask is a
+ * constant of the forward (no gradient). dq [B,H,Lq,D], dk/dv [B,H,Lk,D]. */
+uint32_t oracle_mha_bwd(const double* q, const double* k, const double* v, const double* dout,
+                        const int32_t* lens, const double* add, unsigned kind, int B, int H,
+                        int Lq, int Lk, int D, double scale, double* dq, double* dk,
+                        double* dv) {
+    uint32_t flags = length_flags(kind, lens, B, Lk);
+#pragma omp parallel reduction(| : flags)
+    {
+        size_t n = (size_t)(Lk > 0 ? Lk : 1);
+        double* s = (double*)malloc(sizeof(double) * n);
+        double* p = (double*)malloc(sizeof(double) * n);
+        double* dp = (double*)malloc(sizeof(double) * n);
+        double* o = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+            int64_t b = bh / H, h = bh % H;
+            const double* K = k + bh * Lk * D;
+            const double* V = v + bh * Lk * D;
+            double* dK = dk + bh * Lk * D;
+            double* dV = dv + bh * Lk * D;
+            for (int64_t e = 0; e < (int64_t)Lk * D; ++e) dK[e] = dV[e] = 0.0;
+            int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
+            for (int64_t i = 0; i < Lq; ++i) {
+                const double* qi = q + (bh * Lq + i) * D;
+                const double* gi = dout + (bh * Lq + i) * D;
+                double* dqi = dq + (bh * Lq + i) * D;
+                const double* addrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
+                flags |= attention_row(qi, K, V, Lk, D, scale, kind, i, len_b, addrow, s, p, o);
+                for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+                /* dP over the legal keys, and sum_k p_k dP_k */
+                double c = 0.0;
+                for (int j = 0; j < Lk; ++j) {
+                    if (s[j] == -INFINITY) continue;
+                    double t = 0.0;
+                    for (int d = 0; d < D; ++d) t += gi[d] * V[(int64_t)j * D + d];
+                    dp[j] = t;
+                    c += p[j] * t;
+                }
+                for (int j = 0; j < Lk; ++j) {
+                    if (s[j] == -INFINITY) continue;
+                    double ds = p[j] * (dp[j] - c);
+                    for (int d = 0; d < D; ++d) {
+                        dqi[d] += scale * ds * K[(int64_t)j * D + d];
+                        dK[(int64_t)j * D + d] += scale * ds * qi[d];
+                        dV[(int64_t)j * D + d] += p[j] * gi[d];
+                    }
+                }
+            }
+        }
+        free(s);
+        free(p);
+        free(dp);
+        free(o);
     }
     return flags;
 }
