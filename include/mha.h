@@ -10,7 +10,7 @@
  *           kernel?" (cms365.cn question page)
  *
  * One call is one kernel launch on the caller's stream (decode: at most two,
- * see mha_decode_fwd). Inside it, for every
+ * see mha_decode_fwd; backward: two). Inside it, for every
  * (batch, head, query) row: S = scale * Q K^T, a causal / key-padding /
  * additive mask applied before normalisation, a numerically stable online
  * softmax (running row max, rescaled running sum), and P V accumulated in
@@ -189,6 +189,32 @@ mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int
  * same shape/dtype status codes as mha_decode_fwd. */
 mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
                                      size_t* bytes);
+
+/* Backward of mha_fwd: the gradients of the attention output for an
+ * upstream gradient dout [MAX 3.3: the softmax Jacobian dp_j/ds_k =
+ * p_j (delta_jk - p_k); the row maximum carries no gradient]:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+ *   dQ = scale dS K,  dK = scale dS^T Q,   with P the forward's softmax
+ *   weights over the legal keys (rebuilt in the kernels from each row's
+ *   log-sum-exp; 0 for masked keys). The forward's output is not needed.
+ *   q, dout, dq [B,H,Lq,D];  k, v, dk, dv [B,H,Lk,D]
+ *   mask, mask_kind: NONE, CAUSAL, PADDING (int32 lengths [B]) or
+ *         CAUSAL|PADDING as in mha_fwd; tensor masks give MHA_E_UNSUPPORTED.
+ *   dtype: MHA_F16 or MHA_BF16 (MHA_F32 gives MHA_E_UNSUPPORTED); D must be
+ *         32, 64 or 128 (16 gives MHA_E_UNSUPPORTED).
+ *   workspace: at least mha_bwd_workspace_size(...) bytes, 16-byte aligned,
+ *         owned by the caller (each row's log-sum-exp and rowsum(P * dP));
+ *         no initialisation needed; overlapping calls must not share it.
+ * A fully masked query row has dq = 0 and contributes nothing to dk, dv; it
+ * raises MHA_FLAG_FULLY_MASKED_ROW. Two launches on `stream` (dq, then dk and
+ * dv). Validation, errors and flags as mha_fwd. */
+mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout,
+                   const void* mask, unsigned mask_kind, int B, int H, int Lq, int Lk, int D,
+                   float scale, mha_dtype dtype, void* workspace, size_t workspace_bytes,
+                   void* stream, void* dq, void* dk, void* dv);
+
+/* Workspace bytes mha_bwd needs: 8 * B * H * Lq. Pure host computation. */
+mha_status mha_bwd_workspace_size(int B, int H, int Lq, mha_dtype dtype, size_t* bytes);
 
 /* Debug counters [MAX 6: count executions with device atomics]: a device
  * pointer to 3 uint64 values, or NULL to stop counting. While set, every

@@ -16,6 +16,7 @@ from ._abi import (ADDITIVE, BF16, CAUSAL, F16, F32, FLAG_BAD_LENGTH, FLAG_FULLY
                    FLAG_NONFINITE, KEEP, MASK_NONE, PADDING, PER_HEAD, MhaError, check, lib)
 
 __all__ = ["fwd", "prenorm_cross_fwd", "softmax_rows", "decode", "decode_workspace_size",
+           "bwd", "bwd_workspace_size",
            "get_flags", "set_debug_counters",
            "tile_config", "init", "MhaError", "CAUSAL", "PADDING", "ADDITIVE", "KEEP", "PER_HEAD",
            "MASK_NONE",
@@ -181,6 +182,49 @@ def decode(q, k, v, lens=None, scale: Optional[float] = None, out=None, lse=None
                               _ptr(workspace), ws_bytes, _stream(stream), _ptr(out), _ptr(lse))
     check(st, "mha_decode_fwd")
     return out, lse
+
+
+def bwd_workspace_size(B: int, H: int, Lq: int, dtype_code: int) -> int:
+    """Bytes of device workspace that bwd needs (the rows' statistics)."""
+    n = ctypes.c_size_t(0)
+    check(lib().mha_bwd_workspace_size(B, H, Lq, dtype_code, ctypes.byref(n)),
+          "mha_bwd_workspace_size")
+    return int(n.value)
+
+
+def bwd(q, k, v, dout, mask=None, kind: int = MASK_NONE, scale: Optional[float] = None,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of fwd for the upstream gradient dout: q, dout [B,H,Lq,D],
+    k, v [B,H,Lk,D] -> (dq, dk, dv). ``workspace`` is a uint8 GPU tensor of at least
+    bwd_workspace_size(...) bytes; when omitted one is allocated here."""
+    torch = _torch()
+    _dev(q, "q")
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    _dev(k, "k", q.dtype, (B, H, Lk, D))
+    _dev(v, "v", q.dtype, (B, H, Lk, D))
+    _dev(dout, "dout", q.dtype, (B, H, Lq, D))
+    m = _mask_arg(mask, kind, B, H, Lq, Lk, q.dtype)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _dev(dq, "dq", q.dtype, (B, H, Lq, D))
+    _dev(dk, "dk", q.dtype, (B, H, Lk, D))
+    _dev(dv, "dv", q.dtype, (B, H, Lk, D))
+    code = _dtype_code(q)
+    need = bwd_workspace_size(B, H, Lq, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().mha_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(m), kind, B, H, Lq, Lk, D,
+                       scale, code, _ptr(workspace), ws_bytes, _stream(stream), _ptr(dq), _ptr(dk),
+                       _ptr(dv))
+    check(st, "mha_bwd")
+    return dq, dk, dv
 
 
 def get_flags(clear: bool = True, stream=None) -> int:

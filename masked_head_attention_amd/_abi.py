@@ -33,6 +33,9 @@ SIGNATURES = {
     "mha_decode_fwd": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, ctypes.c_size_t, _vp,
                         _vp, _vp], _i),
     "mha_decode_workspace_size": ([_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)], _i),
+    "mha_bwd": ([_vp, _vp, _vp, _vp, _vp, _u, _i, _i, _i, _i, _i, _f, _i, _vp, ctypes.c_size_t,
+                 _vp, _vp, _vp, _vp], _i),
+    "mha_bwd_workspace_size": ([_i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)], _i),
 }
 
 _lib = None

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["mha_api.hip", "mha_inst_f32.hip", "mha_inst_f16.hip", "mha_inst_bf16.hip",
-           "mha_softmax.hip", "mha_decode.hip"]
+           "mha_softmax.hip", "mha_decode.hip", "mha_bwd.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
          "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
          f"-I{CSRC}"]

@@ -14,6 +14,7 @@
 
 #include "mha.h"
 #include "mha_launch.hpp"
+#include "mha_bwd.hpp"
 #include "mha_decode.hpp"
 #include "mha_softmax.hpp"
 
@@ -21,6 +22,7 @@ namespace mha {
 hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, bool vec_ok, hipStream_t s);
 void decode_plan(int B, int H, int Lk, int D, int esize, int* chunk, int* nsplit);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int dtype, int D, hipStream_t s);
 }
 
 namespace {
@@ -187,6 +189,74 @@ mha_status decode_check(int B, int H, int Lk, int D, mha_dtype dtype, int* chunk
 }  // namespace
 
 extern "C" {
+
+mha_status mha_bwd_workspace_size(int B, int H, int Lq, mha_dtype dtype, size_t* bytes) {
+  if (!bytes) return MHA_E_NULL;
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (B < 0 || H < 0 || Lq < 0) return MHA_E_SHAPE;
+  if (!count_ok({B, H, Lq}, 8)) return MHA_E_OVERFLOW;
+  *bytes = (size_t)B * H * Lq * 8;  // each row's log-sum-exp and sum_j P dP, float32
+  return MHA_OK;
+}
+
+mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout,
+                   const void* mask, unsigned mask_kind, int B, int H, int Lq,
+                   int Lk, int D, float scale, mha_dtype dtype, void* workspace,
+                   size_t workspace_bytes, void* stream, void* dq, void* dk, void* dv) {
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (mask_kind & ~31u) return MHA_E_MASK;
+  if (mask_kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP | MHA_MASK_PER_HEAD))
+    return MHA_E_UNSUPPORTED;
+  const bool pad = (mask_kind & MHA_MASK_PADDING) != 0;
+  if (!pad && mask) return MHA_E_MASK;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return MHA_E_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
+  if (dtype == MHA_F32 || D == 16) return MHA_E_UNSUPPORTED;
+  if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
+  if (B == 0 || H == 0 || (Lq == 0 && Lk == 0)) return MHA_OK;  // empty call
+  if (pad && !mask) return MHA_E_NULL;
+  if (!dk || !dv || (Lk > 0 && (!k || !v))) return MHA_E_NULL;
+  if (Lq > 0 && (!q || !dout || !dq)) return MHA_E_NULL;
+  const void* ptrs16[] = {q, k, v, dout, dq, dk, dv};
+  for (const void* p : ptrs16)
+    if (p && !aligned(p, 16)) return MHA_E_ALIGN;
+  if (pad && !aligned(mask, 4)) return MHA_E_ALIGN;
+  if (!count_ok({B, H, Lq, D}, 2) || !count_ok({B, H, Lk, D}, 2)) return MHA_E_OVERFLOW;
+  if (((int64_t)Lq + 256) * D * 2 > 0xFFFFFFFFLL || ((int64_t)Lk + 256) * D * 2 > 0xFFFFFFFFLL)
+    return MHA_E_OVERFLOW;
+  const int64_t nq = (Lq + 31) / 32, nk = (Lk + 31) / 32;
+  if ((int64_t)B * H * nq > 0x7fffffffLL || (int64_t)B * H * nk > 0x7fffffffLL)
+    return MHA_E_OVERFLOW;
+  const size_t ws = (size_t)B * H * Lq * 8;
+  if (ws > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < ws))
+    return MHA_E_WORKSPACE;
+  uint32_t* flags = nullptr;
+  mha_status st = device_flags(&flags);
+  if (st != MHA_OK) return st;
+  mha::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.lens = pad ? static_cast<const int32_t*>(mask) : nullptr;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.lse2 = static_cast<float*>(workspace);
+  p.delta = p.lse2 ? p.lse2 + (int64_t)B * H * Lq : nullptr;
+  p.B = B;
+  p.H = H;
+  p.Lq = Lq;
+  p.Lk = Lk;
+  p.nqblk = (int)nq;
+  p.nkblk = (int)nk;
+  p.causal = (mask_kind & MHA_MASK_CAUSAL) != 0;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.scale = scale;
+  p.flags = flags;
+  const hipError_t e = mha::launch_bwd(p, (int)dtype, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
+}
 
 mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
                                      size_t* bytes) {

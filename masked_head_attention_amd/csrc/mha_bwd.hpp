@@ -1,0 +1,364 @@
+// mha_bwd.hpp -- backward of the fused masked multi-head attention forward for
+// gfx950 (CDNA4), float16 and bfloat16: the gradients dQ, dK, dV for an
+// upstream gradient dO.
+//
+// Source (web page, cited by title and section):
+//   [MAX] "Why attention must compute the max first" (gsyq.cn/news/340375),
+//         3.3: the softmax Jacobian dp_j/ds_k = p_j (delta_jk - p_k); the row
+//         maximum carries no gradient, so the weights can be rebuilt from the
+//         row's log-sum-exp.
+// With P = softmax(scale Q K^T) over the legal keys:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),
+//   Delta_i = sum_j P_ij dP_ij (the Jacobian's row term),  dQ = scale dS K,
+//   dK = scale dS^T Q.
+//
+// Two kernels, one wave per 32-row block, all contractions on 32x32x16 MFMA
+// with float32 accumulation:
+//   * dq kernel (a query block): pass 1 computes each row's log-sum-exp from
+//     S^T = K Q^T and, with dP^T = V dO^T, Delta (a running maximum with the
+//     rescaled sums of the weights and of weight * dP per lane, as in the
+//     forward's online softmax); pass 2 rebuilds P and dP, forms dS and
+//     accumulates dQ = dS K. It also stores the log-sum-exp and Delta of
+//     each row for the second kernel. Delta is formed from P and dP in
+//     float32, not from the stored 16-bit output O (whose rounding would
+//     shift every dS of a row).
+//   * dkv kernel (a key block): S = Q K^T and dP = dO V^T per query tile,
+//     P from the stored log-sum-exp, then dV += P^T dO and dK += dS^T Q.
+// Operand layouts (32x32x16 MFMA): lane l supplies row/column l % 32 and the
+// 8 consecutive k-slots 8 (l / 32) .. +7; accumulator register i of lane l
+// holds row 8 (i / 4) + 4 (l / 32) + i % 4 of column l % 32. Rows of a
+// score tile are loaded through keymap (mha_common.hpp), so a lane's 16
+// score accumulators are two runs of 8 consecutive keys (or queries): they
+// are the k-slots of the next contraction's A operand as they stand. The B
+// operands that need 8 consecutive rows of one feature (K for dQ, dO and Q
+// for dV and dK) go through a transposed copy of the tile in LDS.
+// P and dS enter the MFMAs as a pair of 16-bit values (the rounded value
+// and the rounded remainder), so the products keep about 16 significant
+// bits beyond the 16-bit type.
+#pragma once
+
+#include "mha_common.hpp"
+
+namespace mha {
+
+struct BwdParams {
+  const void* q;        // [B,H,Lq,D]
+  const void* k;        // [B,H,Lk,D]
+  const void* v;        // [B,H,Lk,D]
+  const void* dout;     // [B,H,Lq,D]
+  const int32_t* lens;  // [B] (PADDING) or null
+  void* dq;             // [B,H,Lq,D]
+  void* dk;             // [B,H,Lk,D]
+  void* dv;             // [B,H,Lk,D]
+  float* lse2;          // [B*H*Lq] row log-sum-exp, log2 units of c*q.k (workspace)
+  float* delta;         // [B*H*Lq] sum_j P_ij dP_ij (workspace)
+  int B, H, Lq, Lk;
+  int nqblk, nkblk;     // 32-row blocks of queries and of keys
+  int causal;
+  float c;              // scale * log2(e)
+  float scale;
+  uint32_t* flags;
+};
+
+// Key (or query) offset within a 32-row tile held by accumulator register i
+// of a lane in half hh, for a tile whose rows were loaded through keymap.
+__device__ inline int run_off(int i, int hh) { return i < 8 ? 8 * hh + i : 16 + 8 * hh + (i - 8); }
+
+// A operand frag (k-block kk of a 32-wide contraction) from accumulator
+// values: registers 8kk .. 8kk+7, as the rounded value and its remainder.
+template <typename T>
+__device__ inline void split_frag(const float* x, Frag8<T>& hi, Frag8<T>& lo) {
+  float h[8], r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (float)(T)x[e];
+    r[e] = x[e] - h[e];
+  }
+  hi = pack8<T>(h);
+  lo = pack8<T>(r);
+}
+
+// LDS tile stored transposed: element (row, f) at t[f * TS + row], 32 rows
+// plus padding per feature.
+constexpr int TS = 40;
+
+// Writes a lane's 16-byte pieces of a 32-row tile (row keymap(l % 32),
+// features 16 kb + 8 hh .. +7) into the transposed LDS tile.
+template <typename T, int D>
+__device__ inline void store_transposed(uint16_t* t, const Frag8<T> (&f)[D / 16], int n, int hh) {
+  const int row = keymap(n);
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    const uint32_t w[4] = {f[kb].u[0].x, f[kb].u[0].y, f[kb].u[0].z, f[kb].u[0].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int feat = 16 * kb + 8 * hh + e;
+      t[feat * TS + row] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// B operand frag: feature 32 fb + n, rows 16 kk + 8 hh .. +7 of the tile.
+template <typename T>
+__device__ inline Frag8<T> load_transposed(const uint16_t* t, int fb, int kk, int n, int hh) {
+  Frag8<T> f;
+  f.u[0] = *reinterpret_cast<const uint4*>(t + (32 * fb + n) * TS + 16 * kk + 8 * hh);
+  return f;
+}
+
+template <typename T, int D>
+__device__ inline void load_rows(const __amdgpu_buffer_rsrc_t rs, int row, int hh,
+                                 Frag8<T> (&f)[D / 16]) {
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb)
+    f[kb].u[0] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                   rs, (uint32_t)row * (D * 2) + (16 * kb + 8 * hh) * 2, 0, 0));
+}
+
+__device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
+  if (!p.lens) {
+    *bad = false;
+    return p.Lk;
+  }
+  const int l = p.lens[b];
+  *bad = l < 0 || l > p.Lk;
+  return l < 0 ? 0 : (l > p.Lk ? p.Lk : l);
+}
+
+// ---- dQ (and the row statistics) per 32-query block ----------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[D * TS];
+  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
+  const int bh = blockIdx.x / p.nqblk;
+  const int q0 = (blockIdx.x - bh * p.nqblk) * 32;
+  bool bad = false;
+  const int kend = bwd_len(p, bh / p.H, &bad);
+  const int qi = q0 + n;  // this lane's query (column of S^T)
+  const int64_t qoff = (int64_t)bh * p.Lq * D * 2, koff = (int64_t)bh * p.Lk * D * 2;
+  const uint32_t qbytes = (uint32_t)p.Lq * D * 2;
+  const auto qrs = make_rsrc(static_cast<const char*>(p.q) + qoff, qbytes);
+  const auto grs = make_rsrc(static_cast<const char*>(p.dout) + qoff, qbytes);
+  const auto krs = make_rsrc(static_cast<const char*>(p.k) + koff, (uint32_t)kend * D * 2);
+  const auto vrs = make_rsrc(static_cast<const char*>(p.v) + koff, (uint32_t)kend * D * 2);
+
+  Frag8<T> qf[D / 16], gf[D / 16];
+  load_rows<T, D>(qrs, qi, hh, qf);
+  load_rows<T, D>(grs, qi, hh, gf);
+  // keys past the block's last query are illegal for all its rows (causal)
+  const int kmax = p.causal ? min(kend, q0 + 32) : kend;
+  const int ntile = (kmax + 31) / 32;
+
+  // S^T and dP^T of key tile t (K and V rows loaded through keymap)
+  auto tile = [&](int t, Frag8<T> (&kf)[D / 16], f32x16& sa, f32x16& da) {
+    Frag8<T> vf[D / 16];
+    load_rows<T, D>(krs, 32 * t + keymap(n), hh, kf);
+    load_rows<T, D>(vrs, 32 * t + keymap(n), hh, vf);
+    sa = f32x16{};
+    da = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      sa = mma8(kf[kb], qf[kb], sa);
+      da = mma8(vf[kb], gf[kb], da);
+    }
+  };
+  auto legal = [&](int key) { return key < kend && !(p.causal && key > qi); };
+
+  // pass 1: log-sum-exp (log2 units) and Delta = sum_j P_j dP_j of each row:
+  // running maximum m, sum l of 2^(s - m) and sum a of 2^(s - m) dP
+  float m = -INFINITY, l = 0.f, a = 0.f;
+  for (int t = 0; t < ntile; ++t) {
+    Frag8<T> kf[D / 16];
+    f32x16 sa, da;
+    tile(t, kf, sa, da);
+    float s[16], mx = m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = legal(32 * t + run_off(i, hh)) ? sa[i] * p.c : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    const float alpha = exp2_fast(m - mu);
+    l *= alpha;
+    a *= alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = exp2_fast(s[i] - mu);
+      l += e;
+      a = __builtin_fmaf(e, da[i], a);
+    }
+    m = mx;
+  }
+  const float M = pair_max(m);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  const float w = exp2_fast(m - Mu);
+  const float L = pair_sum(l * w);
+  const float A = pair_sum(a * w);
+  const float lse = (L == 0.f) ? -INFINITY : Mu + __log2f(L);
+  const float delta = (L == 0.f) ? 0.f : A / L;
+  const bool row_ok = qi < p.Lq;
+  if (hh == 0 && row_ok) {
+    p.lse2[(int64_t)bh * p.Lq + qi] = lse;
+    p.delta[(int64_t)bh * p.Lq + qi] = delta;
+  }
+
+  // pass 2: dS and dQ = dS K
+  f32x16 dqa[D / 32];
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb) dqa[fb] = f32x16{};
+  for (int t = 0; t < ntile; ++t) {
+    Frag8<T> kf[D / 16];
+    f32x16 sa, da;
+    tile(t, kf, sa, da);
+    __syncthreads();  // the previous tile's reads of kt are done
+    store_transposed<T, D>(kt, kf, n, hh);
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pr =
+          (legal(32 * t + run_off(i, hh)) && lse != -INFINITY) ? exp2_fast(sa[i] * p.c - lse) : 0.f;
+      ds[i] = pr * (da[i] - delta);
+    }
+    __syncthreads();  // kt holds the tile
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      Frag8<T> hi, lo;
+      split_frag<T>(ds + 8 * kk, hi, lo);
+#pragma unroll
+      for (int fb = 0; fb < D / 32; ++fb) {
+        const Frag8<T> kb = load_transposed<T>(kt, fb, kk, n, hh);
+        dqa[fb] = mma8(hi, kb, dqa[fb]);
+        dqa[fb] = mma8(lo, kb, dqa[fb]);
+      }
+    }
+  }
+  // dQ: lane holds feature 32 fb + n of rows 8 (i / 4) + 4 hh + i % 4
+  T* dq = static_cast<T*>(p.dq) + (int64_t)bh * p.Lq * D;
+  bool nonfinite = false;
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (row < p.Lq) {
+        const T y = (T)(dqa[fb][i] * p.scale);
+        dq[(int64_t)row * D + 32 * fb + n] = y;
+        nonfinite |= !__builtin_isfinite((float)y);
+      }
+    }
+  const bool empty_row = row_ok && lse == -INFINITY;
+  const uint64_t nf = __ballot(nonfinite), em = __ballot(empty_row);
+  if (lane == 0) {
+    const uint32_t fl = (nf ? F_NONFINITE : 0u) | (em ? F_FULLY_MASKED_ROW : 0u) |
+                        (bad ? F_BAD_LENGTH : 0u);
+    if (fl) atomicOr(p.flags, fl);
+  }
+}
+
+// ---- dK and dV per 32-key block -----------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t qt[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[D * TS];
+  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
+  const int bh = blockIdx.x / p.nkblk;
+  const int k0 = (blockIdx.x - bh * p.nkblk) * 32;
+  bool bad = false;
+  const int kend = bwd_len(p, bh / p.H, &bad);
+  const int kj = k0 + n;  // this lane's key (column of S)
+  const int64_t qoff = (int64_t)bh * p.Lq * D * 2, koff = (int64_t)bh * p.Lk * D * 2;
+  const uint32_t qbytes = (uint32_t)p.Lq * D * 2;
+  const auto qrs = make_rsrc(static_cast<const char*>(p.q) + qoff, qbytes);
+  const auto grs = make_rsrc(static_cast<const char*>(p.dout) + qoff, qbytes);
+  const auto krs = make_rsrc(static_cast<const char*>(p.k) + koff, (uint32_t)kend * D * 2);
+  const auto vrs = make_rsrc(static_cast<const char*>(p.v) + koff, (uint32_t)kend * D * 2);
+  const float* lse2 = p.lse2 + (int64_t)bh * p.Lq;
+  const float* dlt = p.delta + (int64_t)bh * p.Lq;
+
+  Frag8<T> kf[D / 16], vf[D / 16];
+  load_rows<T, D>(krs, kj, hh, kf);
+  load_rows<T, D>(vrs, kj, hh, vf);
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb) dka[fb] = dva[fb] = f32x16{};
+
+  // queries before the block's first key see none of its keys (causal)
+  const int t0 = p.causal ? k0 / 32 : 0;
+  const int ntile = k0 < kend ? (p.Lq + 31) / 32 : 0;  // a padded block gets zeros
+  for (int t = t0; t < ntile; ++t) {
+    Frag8<T> qa[D / 16], ga[D / 16];
+    load_rows<T, D>(qrs, 32 * t + keymap(n), hh, qa);
+    load_rows<T, D>(grs, 32 * t + keymap(n), hh, ga);
+    float lrow[16], drow[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * t + run_off(i, hh);
+      lrow[i] = row < p.Lq ? lse2[row] : -INFINITY;
+      drow[i] = row < p.Lq ? dlt[row] : 0.f;
+    }
+    f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      sa = mma8(qa[kb], kf[kb], sa);
+      da = mma8(ga[kb], vf[kb], da);
+    }
+    __syncthreads();  // the previous tile's reads of qt, gt are done
+    store_transposed<T, D>(qt, qa, n, hh);
+    store_transposed<T, D>(gt, ga, n, hh);
+    float pr[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * t + run_off(i, hh);
+      const bool ok = kj < kend && !(p.causal && kj > row) && lrow[i] != -INFINITY;
+      pr[i] = ok ? exp2_fast(sa[i] * p.c - lrow[i]) : 0.f;
+      ds[i] = pr[i] * (da[i] - drow[i]);
+    }
+    __syncthreads();  // qt, gt hold the tile
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      Frag8<T> phi, plo, shi, slo;
+      split_frag<T>(pr + 8 * kk, phi, plo);
+      split_frag<T>(ds + 8 * kk, shi, slo);
+#pragma unroll
+      for (int fb = 0; fb < D / 32; ++fb) {
+        const Frag8<T> gb = load_transposed<T>(gt, fb, kk, n, hh);
+        dva[fb] = mma8(phi, gb, dva[fb]);
+        dva[fb] = mma8(plo, gb, dva[fb]);
+        const Frag8<T> qb = load_transposed<T>(qt, fb, kk, n, hh);
+        dka[fb] = mma8(shi, qb, dka[fb]);
+        dka[fb] = mma8(slo, qb, dka[fb]);
+      }
+    }
+  }
+  // lane holds feature 32 fb + n of keys 8 (i / 4) + 4 hh + i % 4
+  T* dk = static_cast<T*>(p.dk) + (int64_t)bh * p.Lk * D;
+  T* dv = static_cast<T*>(p.dv) + (int64_t)bh * p.Lk * D;
+  bool nonfinite = false;
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (key < p.Lk) {
+        const T a = (T)(dka[fb][i] * p.scale), b = (T)dva[fb][i];
+        dk[(int64_t)key * D + 32 * fb + n] = a;
+        dv[(int64_t)key * D + 32 * fb + n] = b;
+        nonfinite |= !__builtin_isfinite((float)a) || !__builtin_isfinite((float)b);
+      }
+    }
+  if (__ballot(nonfinite) && lane == 0) atomicOr(p.flags, F_NONFINITE);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const long long gq = (long long)p.B * p.H * p.nqblk, gk = (long long)p.B * p.H * p.nkblk;
+  if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (gq > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)gq), dim3(64), 0, stream, p);
+  if (gk > 0)
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3((unsigned)gk), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mha

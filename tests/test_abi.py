@@ -212,3 +212,42 @@ def test_decode_workspace_size():
     assert _ws(1, 1, 10, 48)[0] == "MHA_E_UNSUPPORTED"
     assert _ws(1, 1, 10, 64, dtype=9)[0] == "MHA_E_DTYPE"
     assert _ws(1, -1, 10, 64)[0] == "MHA_E_SHAPE"
+
+
+def _bwd(q=A, k=A, v=A, dout=A, mask=None, kind=0, B=1, H=2, Lq=8, Lk=8, D=64, scale=0.125,
+         dtype=1, ws=A, ws_bytes=1 << 20, dq=A, dk=A, dv=A):
+    return _abi.STATUS[_abi.lib().mha_bwd(q, k, v, dout, mask, kind, B, H, Lq, Lk, D, scale,
+                                          dtype, ws, ws_bytes, None, dq, dk, dv)]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), "MHA_E_DTYPE"),
+    (dict(dtype=0), "MHA_E_UNSUPPORTED"),
+    (dict(D=16), "MHA_E_UNSUPPORTED"),
+    (dict(D=48), "MHA_E_UNSUPPORTED"),
+    (dict(kind=_abi.ADDITIVE, mask=A), "MHA_E_UNSUPPORTED"),
+    (dict(kind=64), "MHA_E_MASK"),
+    (dict(kind=0, mask=A), "MHA_E_MASK"),
+    (dict(kind=_abi.PADDING), "MHA_E_NULL"),
+    (dict(kind=_abi.PADDING, mask=A + 2), "MHA_E_ALIGN"),
+    (dict(B=-1), "MHA_E_SHAPE"),
+    (dict(scale=float("inf")), "MHA_E_ARG"),
+    (dict(dout=None), "MHA_E_NULL"),
+    (dict(dk=None), "MHA_E_NULL"),
+    (dict(dout=A + 8), "MHA_E_ALIGN"),
+    (dict(ws=None), "MHA_E_WORKSPACE"),
+    (dict(ws_bytes=8), "MHA_E_WORKSPACE"),
+    (dict(Lk=1 << 24, D=128), "MHA_E_OVERFLOW"),
+    (dict(B=0), "MHA_OK"),
+    (dict(Lq=0, Lk=0), "MHA_OK"),
+])
+def test_bwd_validation(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    n = ctypes.c_size_t(0)
+    assert _abi.lib().mha_bwd_workspace_size(2, 3, 100, 1, ctypes.byref(n)) == 0
+    assert n.value == 2 * 3 * 100 * 8
+    assert _abi.STATUS[_abi.lib().mha_bwd_workspace_size(2, -3, 100, 1, ctypes.byref(n))] == \
+        "MHA_E_SHAPE"

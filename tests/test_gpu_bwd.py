@@ -1,0 +1,100 @@
+"""GPU parity of the backward (the gradients dQ, dK, dV of the masked
+attention forward for an upstream gradient dO, through the softmax Jacobian of
+"Why attention must compute the max first", section 3.3) against the fp64
+oracle, through the C ABI.
+
+Bar: |gpu - oracle| <= 2e-3 + half an output ulp elementwise for every
+gradient (float16 / bfloat16); flags agree exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import assert_parity, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import masked_head_attention_amd as M
+
+    M.init()
+    M.get_flags(clear=True)
+    yield
+
+
+def _run(w, g):
+    import masked_head_attention_amd as M
+
+    print(f"[bwd] {w.name} {w.dtype} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} D{w.D} kind {w.kind} "
+          f"seed {w.seed}", flush=True)
+    q, k, v = (to_dev(getattr(w, n), w.dtype) for n in ("q", "k", "v"))
+    mask = to_dev(w.lens, w.dtype) if w.kind & W.PADDING else None
+    M.get_flags(clear=True)
+    dq, dk, dv = M.bwd(q, k, v, to_dev(g, w.dtype), mask=mask, kind=w.kind, scale=w.scale)
+    flags = M.get_flags(clear=True)
+    return from_dev(dq), from_dev(dk), from_dev(dv), flags
+
+
+def _check(w, what, std=1.0):
+    g = W.grad_output(w, std)
+    gq, gk, gv, flags = _run(w, g)
+    rq, rk, rv, rflags = oracle.mha_bwd(w.f64("q"), w.f64("k"), w.f64("v"), W.to_f64(g, w.dtype),
+                                        w.kind, w.lens, None, w.scale)
+    for name, a, b in [("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)]:
+        assert_parity(a, b, w.dtype, f"{what} {name}")
+    assert flags == rflags, (what, flags, rflags)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("kind", [0, W.CAUSAL, W.PADDING, W.CAUSAL | W.PADDING])
+def test_bwd_parity(dtype, D, kind):
+    L = 100 if D == 128 else 130
+    lr = (1, L) if kind & W.PADDING else None
+    w = W.make(f"bwd-{dtype}-{D}", dtype, 2, 3, L, L, D, kind=kind, seed=D + kind,
+               lens_range=lr)
+    _check(w, f"bwd-{dtype}-D{D}-kind{kind}")
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (33, 70), (70, 33), (64, 64), (5, 200)])
+def test_bwd_shapes(Lq, Lk):
+    w = W.make("bwd-shapes", "f16", 1, 2, Lq, Lk, 64, seed=Lq * 7 + Lk, qkv_std=1.5)
+    _check(w, f"bwd-shape-{Lq}x{Lk}")
+
+
+def test_bwd_zero_lengths_and_flags():
+    w = W.make("bwd-len0", "bf16", 3, 2, 40, 40, 64, kind=W.PADDING | W.CAUSAL, seed=31,
+               lens_range=(0, 40))
+    w.lens = np.array([0, 40, 17], np.int32)
+    _check(w, "bwd-len0")
+
+
+def test_bwd_large_gradients():
+    w = W.make("bwd-large", "f16", 1, 4, 96, 96, 64, kind=W.CAUSAL, seed=32, qkv_std=2.0)
+    _check(w, "bwd-large", std=4.0)
+
+
+def test_bwd_workload_full_size_sampled():
+    """The backward at the causal Llama-2-7B shape (the benchmark's workload),
+    in the launch configuration the benchmark times: two heads against the
+    oracle, every value finite."""
+    import torch
+
+    w = W.config(W.BWD_CONFIG)
+    g = W.grad_output(w)
+    gq, gk, gv, flags = _run(w, g)
+    assert flags == 0
+    for h in (0, w.H - 1):
+        sl = slice(h, h + 1)
+        rq, rk, rv, _ = oracle.mha_bwd(w.f64("q")[:, sl], w.f64("k")[:, sl], w.f64("v")[:, sl],
+                                       W.to_f64(g, w.dtype)[:, sl], w.kind, None, None, w.scale)
+        for name, a, b in [("dq", gq[:, sl], rq), ("dk", gk[:, sl], rk), ("dv", gv[:, sl], rv)]:
+            assert_parity(a, b, w.dtype, f"bwd-workload head {h} {name}")
+    assert np.isfinite(gq).all() and np.isfinite(gk).all() and np.isfinite(gv).all()
+    del torch

@@ -239,3 +239,17 @@ def decode_config(**overrides) -> Workload:
     if spec.get("Lq", 1) != 1:
         raise ValueError("decode has one query row")
     return make(**spec)
+
+
+# ---- the upstream gradient of the backward -------------------------------------
+def grad_output(w: Workload, std: float = 1.0) -> np.ndarray:
+    """dO for workload w: std * N(0, 1) of the output's shape [B,H,Lq,D], rounded
+    to the workload's dtype, drawn from its own stream default_rng(seed + 7919)
+    so the workload's other tensors are unchanged."""
+    rng = np.random.default_rng(w.seed + 7919)
+    return round_to(_normal(rng, (w.B, w.H, w.Lq, w.D), std), w.dtype)
+
+
+# The backward workload: the gradients of the causal Llama-2-7B-shaped
+# self-attention (workload 3's shapes and draws), dO ~ N(0, 1).
+BWD_CONFIG = 3
