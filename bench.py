@@ -42,6 +42,9 @@ SOFTMAX_CONFIG_ID = 6
 SOFTMAX_KERNEL_NAME = "mha_softmax_rows"
 DECODE_CONFIG_ID = 7
 DECODE_KERNEL_NAME = "mha_decode"
+BWD_CONFIG_ID = 8
+BWD_KERNEL_NAME = "mha_bwd"
+BWD_METRIC = "masked-MHA bwd effective TFLOP/s + µs/call; % of MFMA roofline (1 GPU)"
 SOFTMAX_METRIC = "row softmax of a materialised score tensor: GB/s; % of HBM roofline (1 GPU)"
 
 
@@ -115,6 +118,7 @@ KERNEL_SOURCES = {
                   "mha_inst_bf16.hip", "mha_inst_f16.hip", "mha_inst_f32.hip"),
     SOFTMAX_KERNEL_NAME: ("mha_common.hpp", "mha_softmax.hpp", "mha_softmax.hip"),
     DECODE_KERNEL_NAME: ("mha_common.hpp", "mha_decode.hpp", "mha_decode.hip"),
+    BWD_KERNEL_NAME: ("mha_common.hpp", "mha_bwd.hpp", "mha_bwd.hip"),
 }
 
 
@@ -309,10 +313,12 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
-                    choices=sorted(W.CONFIGS) + [SOFTMAX_CONFIG_ID, DECODE_CONFIG_ID],
+                    choices=sorted(W.CONFIGS) + [SOFTMAX_CONFIG_ID, DECODE_CONFIG_ID,
+                                                 BWD_CONFIG_ID],
                     help=f"workload; {SOFTMAX_CONFIG_ID} = the row softmax of a materialised "
                          f"1x32x2048x2048 float16 score tensor; {DECODE_CONFIG_ID} = decode, one "
-                         "new token per sequence against a float16 H=32 D=128 cache")
+                         "new token per sequence against a float16 H=32 D=128 cache; "
+                         f"{BWD_CONFIG_ID} = the backward of workload 3")
     ap.add_argument("--eager", action="store_true",
                     help="time launch-per-call steps instead of a graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -353,6 +359,8 @@ def main(argv=None):
         return main_softmax(args)
     if args.config == DECODE_CONFIG_ID:
         return main_decode(args)
+    if args.config == BWD_CONFIG_ID:
+        return main_bwd(args)
 
     import masked_head_attention_amd as M
 
@@ -584,6 +592,89 @@ def main_decode(args):
                    "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"},
         "roofline": roof, "cold_cache": cold, "cpu_baseline": cpu, "device_flags": flags,
         "kernel_sources_sha256_16": kernel_source_hash(DECODE_KERNEL_NAME),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def bwd_cpu_baseline(w: W.Workload, g: np.ndarray, pairs_row: np.ndarray, target_s: float):
+    """The fp64 oracle's backward on a random sample of (b, h) heads, repeated
+    to ~target_s; reported as effective TFLOP/s (10 D per legal pair)."""
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    n = min(16, w.B * w.H)
+    idx = rng.choice(w.B * w.H, size=n, replace=False)
+    bs, hs = idx // w.H, idx % w.H
+    q = W.to_f64(w.q[bs, hs][:, None], w.dtype)
+    k = W.to_f64(w.k[bs, hs][:, None], w.dtype)
+    v = W.to_f64(w.v[bs, hs][:, None], w.dtype)
+    go = W.to_f64(g[bs, hs][:, None], w.dtype)
+    lens = None if w.lens is None else np.ascontiguousarray(w.lens[bs])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mha_bwd(q, k, v, go, w.kind, lens, None, w.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    flops = 10.0 * w.D * float(pairs_row[bs].sum()) * reps
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {w.B * w.H} (b,h) heads drawn at random (seed 1234), x{reps}; "
+                      f"{dt:.1f} s of fp64 oracle backward work",
+            "seconds": dt}
+
+
+def main_bwd(args):
+    """The backward workload: one call = dQ, dK, dV of workload 3 (two kernels)."""
+    import torch
+
+    import masked_head_attention_amd as M
+
+    w = W.config(W.BWD_CONFIG)
+    g = W.grad_output(w)
+    fwd_flops, _, pairs_row = work(w)
+    flops = fwd_flops * 10.0 / 4.0  # five products of 2 D per legal pair, not two
+    E = ESIZE[w.dtype]
+    alg_bytes = 7.0 * w.B * w.H * w.Lq * w.D * E  # q, k, v, dO in; dq, dk, dv out (Lq = Lk)
+    d = gpu_setup(w)
+    go = torch.from_numpy(np.ascontiguousarray(g)).cuda()
+    dq, dk, dv = (torch.empty_like(d[n]) for n in ("q", "k", "v"))
+    code = {"f32": M.F32, "f16": M.F16, "bf16": M.BF16}[w.dtype]
+    ws = torch.empty(max(1, M.bwd_workspace_size(w.B, w.H, w.Lq, code)), dtype=torch.uint8,
+                     device="cuda")
+    M.init()
+
+    def step():
+        M.bwd(d["q"], d["k"], d["v"], go, mask=d["mask"], kind=w.kind, scale=w.scale, dq=dq,
+              dk=dk, dv=dv, workspace=ws)
+
+    M.get_flags(clear=True)
+    t_step = time_gpu(step, args.steps, args.warmup, args.eager)
+    t_eager = t_step if args.eager else time_gpu(step, min(args.steps, 100), 5, True)
+    flags = M.get_flags(clear=True)
+    roof = {"bound": "mfma", "achieved": flops / t_step / 1e12, "peak": PEAK_TFLOPS[w.dtype],
+            "unit": "TFLOP/s", "frac": flops / t_step / 1e12 / PEAK_TFLOPS[w.dtype],
+            "traffic": stored_counter(w.name + "-bwd", kernel=BWD_KERNEL_NAME),
+            "timed": "whole call (dq kernel + dkv kernel)"}
+    executed = stored_counter(w.name + "-bwd", "executed_mfma_flops_per_launch",
+                              kernel=BWD_KERNEL_NAME)
+    if executed is not None:
+        roof["executed_mfma_frac"] = executed / t_step / 1e12 / PEAK_TFLOPS[w.dtype]
+    cpu = None if args.no_cpu_baseline else bwd_cpu_baseline(w, g, pairs_row, args.cpu_seconds)
+    line = {
+        "metric": BWD_METRIC, "value": flops / t_step / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
+        "us_per_call": t_step * 1e6, "eager_us_per_call": t_eager * 1e6,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded, workloads.py recipe)",
+        "config": {"workload": w.name + "-bwd", "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk,
+                   "D": w.D, "mask": "causal", "seed": w.seed, "effective_flops": flops,
+                   "algorithmic_bytes": alg_bytes,
+                   "timing": "eager launches" if args.eager else "HIP graph replay of the K steps"},
+        "roofline": roof, "cpu_baseline": cpu, "device_flags": flags,
+        "kernel_sources_sha256_16": kernel_source_hash(BWD_KERNEL_NAME),
     }
     print(json.dumps(line))
     return 0

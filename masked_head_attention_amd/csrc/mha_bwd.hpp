@@ -116,6 +116,23 @@ __device__ inline void load_rows(const __amdgpu_buffer_rsrc_t rs, int row, int h
                    rs, (uint32_t)row * (D * 2) + (16 * kb + 8 * hh) * 2, 0, 0));
 }
 
+// Workgroup -> (head, 32-row block). Workgroups are dealt to the 8 XCDs
+// round-robin; this map keeps every block of a head on one XCD, so the tiles
+// that all blocks of the head stream (K and V, or Q and dO) stay in that
+// XCD's L2. Heads beyond the last complete group of 8 keep the plain order.
+__device__ inline void xcd_block(int nbh, int nblk, int* bh, int* blk) {
+  const int i = blockIdx.x;
+  const int full = (nbh / 8) * 8 * nblk;
+  if (i < full) {
+    const int x = i % 8, j = i / 8;
+    *bh = (j / nblk) * 8 + x;
+    *blk = j % nblk;
+  } else {
+    *bh = i / nblk;
+    *blk = i - *bh * nblk;
+  }
+}
+
 __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
   if (!p.lens) {
     *bad = false;
@@ -131,8 +148,10 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[D * TS];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.x / p.nqblk;
-  const int q0 = (blockIdx.x - bh * p.nqblk) * 32;
+  int bh = 0, qb = 0;
+  xcd_block(p.B * p.H, p.nqblk, &bh, &qb);
+  if (p.causal) qb = p.nqblk - 1 - qb;  // the longest rows (most key tiles) first
+  const int q0 = qb * 32;
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int qi = q0 + n;  // this lane's query (column of S^T)
@@ -262,8 +281,9 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t qt[D * TS];
   __shared__ __attribute__((aligned(16))) uint16_t gt[D * TS];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.x / p.nkblk;
-  const int k0 = (blockIdx.x - bh * p.nkblk) * 32;
+  int bh = 0, kb0 = 0;
+  xcd_block(p.B * p.H, p.nkblk, &bh, &kb0);
+  const int k0 = kb0 * 32;
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int kj = k0 + n;  // this lane's key (column of S)
