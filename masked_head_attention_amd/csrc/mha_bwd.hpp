@@ -169,11 +169,17 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   const int kmax = p.causal ? min(kend, q0 + 32) : kend;
   const int ntile = (kmax + 31) / 32;
 
-  // S^T and dP^T of key tile t (K and V rows loaded through keymap)
-  auto tile = [&](int t, Frag8<T> (&kf)[D / 16], f32x16& sa, f32x16& da) {
-    Frag8<T> vf[D / 16];
-    load_rows<T, D>(krs, 32 * t + keymap(n), hh, kf);
-    load_rows<T, D>(vrs, 32 * t + keymap(n), hh, vf);
+  // K and V rows of key tile t (through keymap). The tile after the last one
+  // is read at rows past the key range: zeros, no memory traffic.
+  const int tpast = (kend + 31) / 32;
+  auto load_kv = [&](int t, Frag8<T> (&kf)[D / 16], Frag8<T> (&vf)[D / 16]) {
+    const int tt = t < ntile ? t : tpast;
+    load_rows<T, D>(krs, 32 * tt + keymap(n), hh, kf);
+    load_rows<T, D>(vrs, 32 * tt + keymap(n), hh, vf);
+  };
+  // S^T and dP^T of a tile
+  auto tile = [&](const Frag8<T> (&kf)[D / 16], const Frag8<T> (&vf)[D / 16], f32x16& sa,
+                  f32x16& da) {
     sa = f32x16{};
     da = f32x16{};
 #pragma unroll
@@ -187,10 +193,15 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   // pass 1: log-sum-exp (log2 units) and Delta = sum_j P_j dP_j of each row:
   // running maximum m, sum l of 2^(s - m) and sum a of 2^(s - m) dP
   float m = -INFINITY, l = 0.f, a = 0.f;
+  Frag8<T> kc[D / 16], vc[D / 16];  // the current tile; the next one is in flight
+  load_kv(0, kc, vc);
   for (int t = 0; t < ntile; ++t) {
-    Frag8<T> kf[D / 16];
+    Frag8<T> kn[D / 16], vn[D / 16];
+    load_kv(t + 1, kn, vn);
     f32x16 sa, da;
-    tile(t, kf, sa, da);
+    tile(kc, vc, sa, da);
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) { kc[kb] = kn[kb]; vc[kb] = vn[kb]; }
     float s[16], mx = m;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -226,12 +237,20 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   f32x16 dqa[D / 32];
 #pragma unroll
   for (int fb = 0; fb < D / 32; ++fb) dqa[fb] = f32x16{};
+  load_kv(0, kc, vc);
   for (int t = 0; t < ntile; ++t) {
-    Frag8<T> kf[D / 16];
+    Frag8<T> kn[D / 16], vn[D / 16];
+    load_kv(t + 1, kn, vn);
     f32x16 sa, da;
-    tile(t, kf, sa, da);
-    __syncthreads();  // the previous tile's reads of kt are done
-    store_transposed<T, D>(kt, kf, n, hh);
+    tile(kc, vc, sa, da);
+    // The workgroup is this one wave: LDS operations complete in order, so
+    // waiting for this wave's own LDS traffic (not its global loads, which
+    // would drain the prefetch) orders the tile's reads and writes across
+    // lanes; the memory clobber keeps the compiler from moving them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous tile's reads are done
+    store_transposed<T, D>(kt, kc, n, hh);
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) { kc[kb] = kn[kb]; vc[kb] = vn[kb]; }
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
           (legal(32 * t + run_off(i, hh)) && lse != -INFINITY) ? exp2_fast(sa[i] * p.c - lse) : 0.f;
       ds[i] = pr * (da[i] - delta);
     }
-    __syncthreads();  // kt holds the tile
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // kt holds the tile
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       Frag8<T> hi, lo;
