@@ -198,8 +198,9 @@ mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtyp
  *   weights over the legal keys (rebuilt in the kernels from each row's
  *   log-sum-exp; 0 for masked keys). The forward's output is not needed.
  *   q, dout, dq [B,H,Lq,D];  k, v, dk, dv [B,H,Lk,D]
- *   mask, mask_kind: NONE, CAUSAL, PADDING (int32 lengths [B]) or
- *         CAUSAL|PADDING as in mha_fwd; tensor masks give MHA_E_UNSUPPORTED.
+ *   mask, mask_kind: every mask kind of mha_fwd (causal, padding lengths,
+ *         additive or keep tensors, shared or PER_HEAD) with the same rules;
+ *         a mask is a constant of the forward and gets no gradient.
  *   dtype: MHA_F16 or MHA_BF16 (MHA_F32 gives MHA_E_UNSUPPORTED); D must be
  *         32, 64 or 128 (16 gives MHA_E_UNSUPPORTED).
  *   workspace: at least mha_bwd_workspace_size(...) bytes, 16-byte aligned,

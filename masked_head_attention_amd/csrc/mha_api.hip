@@ -205,23 +205,27 @@ mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout
                    size_t workspace_bytes, void* stream, void* dq, void* dk, void* dv) {
   if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
   if (mask_kind & ~31u) return MHA_E_MASK;
-  if (mask_kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP | MHA_MASK_PER_HEAD))
-    return MHA_E_UNSUPPORTED;
+  const unsigned tensor = mask_kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP);
+  const unsigned ptr_kinds = mask_kind & (MHA_MASK_PADDING | MHA_MASK_ADDITIVE | MHA_MASK_KEEP);
+  if (ptr_kinds & (ptr_kinds - 1)) return MHA_E_MASK;  // one mask argument
+  if ((mask_kind & MHA_MASK_PER_HEAD) && !tensor) return MHA_E_MASK;
   const bool pad = (mask_kind & MHA_MASK_PADDING) != 0;
-  if (!pad && mask) return MHA_E_MASK;
+  if (!ptr_kinds && mask) return MHA_E_MASK;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return MHA_E_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
   if (dtype == MHA_F32 || D == 16) return MHA_E_UNSUPPORTED;
   if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
   if (B == 0 || H == 0 || (Lq == 0 && Lk == 0)) return MHA_OK;  // empty call
-  if (pad && !mask) return MHA_E_NULL;
+  if (ptr_kinds && !mask) return MHA_E_NULL;
   if (!dk || !dv || (Lk > 0 && (!k || !v))) return MHA_E_NULL;
   if (Lq > 0 && (!q || !dout || !dq)) return MHA_E_NULL;
   const void* ptrs16[] = {q, k, v, dout, dq, dk, dv};
   for (const void* p : ptrs16)
     if (p && !aligned(p, 16)) return MHA_E_ALIGN;
-  if (pad && !aligned(mask, 4)) return MHA_E_ALIGN;
-  if (!count_ok({B, H, Lq, D}, 2) || !count_ok({B, H, Lk, D}, 2)) return MHA_E_OVERFLOW;
+  if ((pad && !aligned(mask, 4)) || (tensor && !aligned(mask, 16))) return MHA_E_ALIGN;
+  if (!count_ok({B, H, Lq, D}, 2) || !count_ok({B, H, Lk, D}, 2) ||
+      !count_ok({B, (mask_kind & MHA_MASK_PER_HEAD) ? H : 1, Lq, Lk}, 2))
+    return MHA_E_OVERFLOW;
   if (((int64_t)Lq + 256) * D * 2 > 0xFFFFFFFFLL || ((int64_t)Lk + 256) * D * 2 > 0xFFFFFFFFLL)
     return MHA_E_OVERFLOW;
   const int64_t nq = (Lq + 31) / 32, nk = (Lk + 31) / 32;
@@ -239,6 +243,9 @@ mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout
   p.v = v;
   p.dout = dout;
   p.lens = pad ? static_cast<const int32_t*>(mask) : nullptr;
+  p.mask = tensor ? mask : nullptr;
+  p.mask_heads = (mask_kind & MHA_MASK_PER_HEAD) ? H : 1;
+  p.keep = (mask_kind & MHA_MASK_KEEP) != 0;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;

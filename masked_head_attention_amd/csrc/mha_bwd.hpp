@@ -47,6 +47,9 @@ struct BwdParams {
   const void* v;        // [B,H,Lk,D]
   const void* dout;     // [B,H,Lq,D]
   const int32_t* lens;  // [B] (PADDING) or null
+  const void* mask;     // [B,Hm,Lq,Lk] additive or keep mask in the element type, or null
+  int mask_heads;       // Hm: 1 (shared by the heads) or H (one slab per head)
+  int keep;             // the mask tensor is a keep-mask (0 masks a key; values not added)
   void* dq;             // [B,H,Lq,D]
   void* dk;             // [B,H,Lk,D]
   void* dv;             // [B,H,Lk,D]
@@ -133,6 +136,25 @@ __device__ inline void xcd_block(int nbh, int nblk, int* bh, int* blk) {
   }
 }
 
+// Entry (row, key) of the head's mask slab as float32 (0 for rows and keys
+// outside the tensor).
+template <typename T>
+__device__ inline float mask_at(const BwdParams& p, int bh, int row, int key) {
+  if (row >= p.Lq || key >= p.Lk) return 0.f;
+  const int64_t slab = p.mask_heads == 1 ? bh / p.H : bh;
+  const uint16_t u =
+      static_cast<const uint16_t*>(p.mask)[(slab * p.Lq + row) * (int64_t)p.Lk + key];
+  T* tag = nullptr;
+  return lo_f((uint32_t)u, tag);
+}
+
+// A legal score in log2 units, or -inf: the mask tensor's decision and (for
+// an additive mask) its value, added after scaling and not scaled.
+__device__ inline float masked_logit(const BwdParams& p, float x, float m) {
+  if (p.keep) return m == 0.f ? -INFINITY : x;
+  return m == -INFINITY ? -INFINITY : __builtin_fmaf(m, 1.4426950408889634f, x);
+}
+
 __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
   if (!p.lens) {
     *bad = false;
@@ -144,7 +166,9 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
 }
 
 // ---- dQ (and the row statistics) per 32-query block ----------------------
-template <typename T, int D>
+// TM: a mask tensor (additive or keep) is read; without one the score path
+// has no per-element mask work.
+template <typename T, int D, bool TM>
 __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[D * TS];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
@@ -205,7 +229,10 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
     float s[16], mx = m;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[i] = legal(32 * t + run_off(i, hh)) ? sa[i] * p.c : -INFINITY;
+      const int key = 32 * t + run_off(i, hh);
+      float x = sa[i] * p.c;
+      if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, qi, key));
+      s[i] = legal(key) ? x : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
     const float mu = (mx == -INFINITY) ? 0.f : mx;
@@ -254,8 +281,11 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pr =
-          (legal(32 * t + run_off(i, hh)) && lse != -INFINITY) ? exp2_fast(sa[i] * p.c - lse) : 0.f;
+      const int key = 32 * t + run_off(i, hh);
+      float x = sa[i] * p.c;
+      if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, qi, key));
+      x = legal(key) ? x : -INFINITY;
+      const float pr = (x != -INFINITY && lse != -INFINITY) ? exp2_fast(x - lse) : 0.f;
       ds[i] = pr * (da[i] - delta);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // kt holds the tile
@@ -295,7 +325,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---- dK and dV per 32-key block -----------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool TM>
 __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t qt[D * TS];
   __shared__ __attribute__((aligned(16))) uint16_t gt[D * TS];
@@ -350,7 +380,10 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
     for (int i = 0; i < 16; ++i) {
       const int row = 32 * t + run_off(i, hh);
       const bool ok = kj < kend && !(p.causal && kj > row) && lrow[i] != -INFINITY;
-      pr[i] = ok ? exp2_fast(sa[i] * p.c - lrow[i]) : 0.f;
+      float x = sa[i] * p.c;
+      if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, row, kj));
+      x = ok ? x : -INFINITY;
+      pr[i] = x != -INFINITY ? exp2_fast(x - lrow[i]) : 0.f;
       ds[i] = pr[i] * (da[i] - drow[i]);
     }
     __syncthreads();  // qt, gt hold the tile
@@ -389,15 +422,20 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
   if (__ballot(nonfinite) && lane == 0) atomicOr(p.flags, F_NONFINITE);
 }
 
-template <typename T, int D>
-hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+template <typename T, int D, bool TM>
+hipError_t launch_bwd_m(const BwdParams& p, hipStream_t stream) {
   const long long gq = (long long)p.B * p.H * p.nqblk, gk = (long long)p.B * p.H * p.nkblk;
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (gq > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((unsigned)gq), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(64), 0, stream, p);
   if (gk > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3((unsigned)gk), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  return p.mask ? launch_bwd_m<T, D, true>(p, stream) : launch_bwd_m<T, D, false>(p, stream);
 }
 
 }  // namespace mha

@@ -225,7 +225,9 @@ def _bwd(q=A, k=A, v=A, dout=A, mask=None, kind=0, B=1, H=2, Lq=8, Lk=8, D=64, s
     (dict(dtype=0), "MHA_E_UNSUPPORTED"),
     (dict(D=16), "MHA_E_UNSUPPORTED"),
     (dict(D=48), "MHA_E_UNSUPPORTED"),
-    (dict(kind=_abi.ADDITIVE, mask=A), "MHA_E_UNSUPPORTED"),
+    (dict(kind=_abi.ADDITIVE | _abi.PADDING, mask=A), "MHA_E_MASK"),
+    (dict(kind=_abi.PER_HEAD), "MHA_E_MASK"),
+    (dict(kind=_abi.KEEP, mask=A + 4), "MHA_E_ALIGN"),
     (dict(kind=64), "MHA_E_MASK"),
     (dict(kind=0, mask=A), "MHA_E_MASK"),
     (dict(kind=_abi.PADDING), "MHA_E_NULL"),

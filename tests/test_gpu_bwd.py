@@ -34,7 +34,8 @@ def _run(w, g):
     print(f"[bwd] {w.name} {w.dtype} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} D{w.D} kind {w.kind} "
           f"seed {w.seed}", flush=True)
     q, k, v = (to_dev(getattr(w, n), w.dtype) for n in ("q", "k", "v"))
-    mask = to_dev(w.lens, w.dtype) if w.kind & W.PADDING else None
+    mask = (to_dev(w.lens, w.dtype) if w.kind & W.PADDING else
+            to_dev(w.add, w.dtype) if w.kind & (W.ADDITIVE | W.KEEP) else None)
     M.get_flags(clear=True)
     dq, dk, dv = M.bwd(q, k, v, to_dev(g, w.dtype), mask=mask, kind=w.kind, scale=w.scale)
     flags = M.get_flags(clear=True)
@@ -45,7 +46,7 @@ def _check(w, what, std=1.0):
     g = W.grad_output(w, std)
     gq, gk, gv, flags = _run(w, g)
     rq, rk, rv, rflags = oracle.mha_bwd(w.f64("q"), w.f64("k"), w.f64("v"), W.to_f64(g, w.dtype),
-                                        w.kind, w.lens, None, w.scale)
+                                        w.kind, w.lens, w.f64("add"), w.scale)
     for name, a, b in [("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)]:
         assert_parity(a, b, w.dtype, f"{what} {name}")
     assert flags == rflags, (what, flags, rflags)
@@ -60,6 +61,17 @@ def test_bwd_parity(dtype, D, kind):
     w = W.make(f"bwd-{dtype}-{D}", dtype, 2, 3, L, L, D, kind=kind, seed=D + kind,
                lens_range=lr)
     _check(w, f"bwd-{dtype}-D{D}-kind{kind}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("kind", [W.ADDITIVE, W.ADDITIVE | W.CAUSAL, W.KEEP,
+                                  W.ADDITIVE | W.PER_HEAD, W.KEEP | W.PER_HEAD | W.CAUSAL])
+def test_bwd_tensor_masks(dtype, kind):
+    """Additive and keep masks, shared or one slab per head, with -inf / 0
+    blocks, key padding folded into the tensor and ragged sizes (Lk odd)."""
+    w = W.make("bwd-masks", dtype, 2, 3, 77, 93, 64, kind=kind, seed=40 + kind,
+               lens_range=(10, 93), block_p=0.25, block=16)
+    _check(w, f"bwd-mask-{dtype}-{kind}")
 
 
 @pytest.mark.parametrize("Lq,Lk", [(1, 1), (33, 70), (70, 33), (64, 64), (5, 200)])
