@@ -282,10 +282,14 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = 32 * t + run_off(i, hh);
-      float x = sa[i] * p.c;
-      if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, qi, key));
-      x = legal(key) ? x : -INFINITY;
-      const float pr = (x != -INFINITY && lse != -INFINITY) ? exp2_fast(x - lse) : 0.f;
+      float pr;
+      if constexpr (TM) {
+        const float x =
+            legal(key) ? masked_logit(p, sa[i] * p.c, mask_at<T>(p, bh, qi, key)) : -INFINITY;
+        pr = (x != -INFINITY && lse != -INFINITY) ? exp2_fast(x - lse) : 0.f;
+      } else {
+        pr = (legal(key) && lse != -INFINITY) ? exp2_fast(sa[i] * p.c - lse) : 0.f;
+      }
       ds[i] = pr * (da[i] - delta);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // kt holds the tile
@@ -380,10 +384,12 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
     for (int i = 0; i < 16; ++i) {
       const int row = 32 * t + run_off(i, hh);
       const bool ok = kj < kend && !(p.causal && kj > row) && lrow[i] != -INFINITY;
-      float x = sa[i] * p.c;
-      if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, row, kj));
-      x = ok ? x : -INFINITY;
-      pr[i] = x != -INFINITY ? exp2_fast(x - lrow[i]) : 0.f;
+      if constexpr (TM) {
+        const float x = ok ? masked_logit(p, sa[i] * p.c, mask_at<T>(p, bh, row, kj)) : -INFINITY;
+        pr[i] = x != -INFINITY ? exp2_fast(x - lrow[i]) : 0.f;
+      } else {
+        pr[i] = ok ? exp2_fast(sa[i] * p.c - lrow[i]) : 0.f;
+      }
       ds[i] = pr[i] * (da[i] - drow[i]);
     }
     __syncthreads();  // qt, gt hold the tile
