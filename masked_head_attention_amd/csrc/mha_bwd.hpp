@@ -31,7 +31,8 @@
 // score accumulators are two runs of 8 consecutive keys (or queries): they
 // are the k-slots of the next contraction's A operand as they stand. The B
 // operands that need 8 consecutive rows of one feature (K for dQ, dO and Q
-// for dV and dK) go through a transposed copy of the tile in LDS.
+// for dV and dK) go through a row-major copy of the tile in LDS, read with
+// the transposing ds_read_b64_tr_b16.
 // P and dS enter the MFMAs as a pair of 16-bit values (the rounded value
 // and the rounded remainder), so the products keep about 16 significant
 // bits beyond the 16-bit type.
@@ -81,31 +82,50 @@ __device__ inline void split_frag(const float* x, Frag8<T>& hi, Frag8<T>& lo) {
   lo = pack8<T>(r);
 }
 
-// LDS tile stored transposed: element (row, f) at t[f * TS + row], 32 rows
-// plus padding per feature.
-constexpr int TS = 40;
+// LDS tiles are row-major, 32 rows of D elements, RS bytes apart: the 32
+// bytes of padding put the 4 rows of one transposed read in different banks.
+template <int D>
+constexpr int tile_rs() { return D * 2 + 32; }
 
 // Writes a lane's 16-byte pieces of a 32-row tile (row keymap(l % 32),
-// features 16 kb + 8 hh .. +7) into the transposed LDS tile.
+// features 16 kb + 8 hh .. +7) into the LDS tile.
 template <typename T, int D>
-__device__ inline void store_transposed(uint16_t* t, const Frag8<T> (&f)[D / 16], int n, int hh) {
-  const int row = keymap(n);
+__device__ inline void store_rows(char* t, const Frag8<T> (&f)[D / 16], int n, int hh) {
+  char* r = t + keymap(n) * tile_rs<D>();
 #pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) {
-    const uint32_t w[4] = {f[kb].u[0].x, f[kb].u[0].y, f[kb].u[0].z, f[kb].u[0].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int feat = 16 * kb + 8 * hh + e;
-      t[feat * TS + row] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-  }
+  for (int kb = 0; kb < D / 16; ++kb)
+    *reinterpret_cast<uint4*>(r + (16 * kb + 8 * hh) * 2) = f[kb].u[0];
 }
 
-// B operand frag: feature 32 fb + n, rows 16 kk + 8 hh .. +7 of the tile.
+typedef __fp16 bwd_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __bf16 bwd_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 template <typename T>
-__device__ inline Frag8<T> load_transposed(const uint16_t* t, int fb, int kk, int n, int hh) {
+__device__ inline uint2 bwd_read_tr(const char* p);
+template <>
+__device__ inline uint2 bwd_read_tr<_Float16>(const char* p) {
+  return __builtin_bit_cast(uint2,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4f16(MHA_LDS_PTR(bwd_f16x4, p)));
+}
+template <>
+__device__ inline uint2 bwd_read_tr<__bf16>(const char* p) {
+  return __builtin_bit_cast(uint2,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(MHA_LDS_PTR(bwd_bf16x4, p)));
+}
+
+// B operand frag: feature 32 fb + l % 32, rows 16 kk + 8 (l / 32) .. +7 of
+// the tile, by two transposing reads. ds_read_b64_tr_b16: within a group of
+// 16 lanes, lane i receives element i % 4 of the 8 bytes addressed by lane
+// 4 j + i / 4 as its element j. Lane 4 j + c addresses row j, features
+// 4 c .. 4 c + 3 of its group's 16, so lane i gets 4 consecutive rows of
+// feature i.
+template <typename T, int D>
+__device__ inline Frag8<T> load_tr_frag(const char* t, int fb, int kk, int lane) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3;
+  const char* a = t + (16 * kk + 8 * (g >> 1) + j) * tile_rs<D>() +
+                  (32 * fb + 16 * (g & 1) + 4 * c) * 2;
+  const uint2 lo = bwd_read_tr<T>(a), hi = bwd_read_tr<T>(a + 4 * tile_rs<D>());
   Frag8<T> f;
-  f.u[0] = *reinterpret_cast<const uint4*>(t + (32 * fb + n) * TS + 16 * kk + 8 * hh);
+  f.u[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
   return f;
 }
 
@@ -170,7 +190,7 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
 // has no per-element mask work.
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t kt[D * TS];
+  __shared__ __attribute__((aligned(16))) char kt[32 * tile_rs<D>()];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
   int bh = 0, qb = 0;
   xcd_block(p.B * p.H, p.nqblk, &bh, &qb);
@@ -275,7 +295,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
     // would drain the prefetch) orders the tile's reads and writes across
     // lanes; the memory clobber keeps the compiler from moving them.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous tile's reads are done
-    store_transposed<T, D>(kt, kc, n, hh);
+    store_rows<T, D>(kt, kc, n, hh);
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) { kc[kb] = kn[kb]; vc[kb] = vn[kb]; }
     float ds[16];
@@ -299,7 +319,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
       split_frag<T>(ds + 8 * kk, hi, lo);
 #pragma unroll
       for (int fb = 0; fb < D / 32; ++fb) {
-        const Frag8<T> kb = load_transposed<T>(kt, fb, kk, n, hh);
+        const Frag8<T> kb = load_tr_frag<T, D>(kt, fb, kk, lane);
         dqa[fb] = mma8(hi, kb, dqa[fb]);
         dqa[fb] = mma8(lo, kb, dqa[fb]);
       }
@@ -331,8 +351,8 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
 // ---- dK and dV per 32-key block -----------------------------------------
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t qt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[D * TS];
+  __shared__ __attribute__((aligned(16))) char qt[32 * tile_rs<D>()];
+  __shared__ __attribute__((aligned(16))) char gt[32 * tile_rs<D>()];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
   int bh = 0, kb0 = 0;
   xcd_block(p.B * p.H, p.nkblk, &bh, &kb0);
@@ -377,8 +397,8 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
       da = mma8(ga[kb], vf[kb], da);
     }
     __syncthreads();  // the previous tile's reads of qt, gt are done
-    store_transposed<T, D>(qt, qa, n, hh);
-    store_transposed<T, D>(gt, ga, n, hh);
+    store_rows<T, D>(qt, qa, n, hh);
+    store_rows<T, D>(gt, ga, n, hh);
     float pr[16], ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -400,10 +420,10 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
       split_frag<T>(ds + 8 * kk, shi, slo);
 #pragma unroll
       for (int fb = 0; fb < D / 32; ++fb) {
-        const Frag8<T> gb = load_transposed<T>(gt, fb, kk, n, hh);
+        const Frag8<T> gb = load_tr_frag<T, D>(gt, fb, kk, lane);
         dva[fb] = mma8(phi, gb, dva[fb]);
         dva[fb] = mma8(plo, gb, dva[fb]);
-        const Frag8<T> qb = load_transposed<T>(qt, fb, kk, n, hh);
+        const Frag8<T> qb = load_tr_frag<T, D>(qt, fb, kk, lane);
         dka[fb] = mma8(shi, qb, dka[fb]);
         dka[fb] = mma8(slo, qb, dka[fb]);
       }
