@@ -68,3 +68,38 @@ def test_kernel_hash_per_family():
         assert len(bench.kernel_source_hash(kernel)) == 16
     assert bench.kernel_source_hash(bench.KERNEL_NAME) != \
         bench.kernel_source_hash(bench.SOFTMAX_KERNEL_NAME)
+
+
+def test_decode_accounting_matches_the_oracle_pairs():
+    """Decode: 4 D FLOPs per legal (key, head) pair, the pairs being those of
+    the one-row forward with key padding; bytes are q and out, K and V of the
+    legal cache rows, the lengths and the float32 LSE."""
+    w = W.decode_config(B=3, H=2, Lk=300, lens_range=(0, 300))
+    w.lens = np.array([0, 300, 117], np.int32)
+    flops, alg = bench.decode_work(w)
+    pairs = oracle.unmasked_pairs(W.PADDING, w.B, w.H, 1, w.Lk, w.lens, None)
+    assert pairs == 2 * (0 + 300 + 117)
+    assert flops == 4.0 * w.D * pairs
+    assert alg == (2 * 3 * 2 * 128 * 2 + 2 * (0 + 300 + 117) * 2 * 128 * 2 + 4 * 3 + 4 * 3 * 2)
+
+
+def test_decode_workload_closed_form():
+    w = W.decode_config()
+    flops, alg = bench.decode_work(w)
+    assert flops == 4 * 128 * 32 * int(w.lens.sum())
+    assert (w.lens >= 256).all() and (w.lens <= 4096).all()
+
+
+def test_backward_flops_are_ten_d_per_pair():
+    # five products of 2 D per legal pair: 2.5 x the forward's 4 D
+    w = W.config(W.BWD_CONFIG)
+    fwd, _, _ = bench.work(w)
+    assert fwd * 10.0 / 4.0 == 10 * 128 * 32 * 2048 * 2049 // 2
+
+
+def test_grad_output_leaves_the_workload_unchanged():
+    a = W.config(1)
+    g = W.grad_output(a)
+    b = W.config(1)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+    assert g.shape == (a.B, a.H, a.Lq, a.D) and np.array_equal(g, W.grad_output(b))
