@@ -7,6 +7,7 @@ namespace mha {
 template <typename T>
 static hipError_t launch_bwd_dtype(const BwdParams& p, int D, hipStream_t s) {
   switch (D) {
+    case 16: return launch_bwd_t<T, 16>(p, s);
     case 32: return launch_bwd_t<T, 32>(p, s);
     case 64: return launch_bwd_t<T, 64>(p, s);
     case 128: return launch_bwd_t<T, 128>(p, s);

@@ -190,6 +190,9 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
 // has no per-element mask work.
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
+  // 32-feature blocks of the dQ accumulators (D = 16: one block whose upper
+  // 16 columns read the LDS tile's row padding and are never stored)
+  constexpr int FB = (D + 31) / 32;
   __shared__ __attribute__((aligned(16))) char kt[32 * tile_rs<D>()];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
   int bh = 0, qb = 0;
@@ -281,9 +284,9 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   }
 
   // pass 2: dS and dQ = dS K
-  f32x16 dqa[D / 32];
+  f32x16 dqa[FB];
 #pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb) dqa[fb] = f32x16{};
+  for (int fb = 0; fb < FB; ++fb) dqa[fb] = f32x16{};
   load_kv(0, kc, vc);
   for (int t = 0; t < ntile; ++t) {
     Frag8<T> kn[D / 16], vn[D / 16];
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
       Frag8<T> hi, lo;
       split_frag<T>(ds + 8 * kk, hi, lo);
 #pragma unroll
-      for (int fb = 0; fb < D / 32; ++fb) {
+      for (int fb = 0; fb < FB; ++fb) {
         const Frag8<T> kb = load_tr_frag<T, D>(kt, fb, kk, lane);
         dqa[fb] = mma8(hi, kb, dqa[fb]);
         dqa[fb] = mma8(lo, kb, dqa[fb]);
@@ -329,11 +332,11 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   T* dq = static_cast<T*>(p.dq) + (int64_t)bh * p.Lq * D;
   bool nonfinite = false;
 #pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb)
+  for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (row < p.Lq) {
+      if (row < p.Lq && 32 * fb + n < D) {
         const T y = (T)(dqa[fb][i] * p.scale);
         dq[(int64_t)row * D + 32 * fb + n] = y;
         nonfinite |= !__builtin_isfinite((float)y);
@@ -351,6 +354,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
 // ---- dK and dV per 32-key block -----------------------------------------
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
+  constexpr int FB = (D + 31) / 32;  // 32-feature blocks of the dK, dV accumulators
   __shared__ __attribute__((aligned(16))) char qt[32 * tile_rs<D>()];
   __shared__ __attribute__((aligned(16))) char gt[32 * tile_rs<D>()];
   const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
@@ -372,9 +376,9 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
   Frag8<T> kf[D / 16], vf[D / 16];
   load_rows<T, D>(krs, kj, hh, kf);
   load_rows<T, D>(vrs, kj, hh, vf);
-  f32x16 dka[D / 32], dva[D / 32];
+  f32x16 dka[FB], dva[FB];
 #pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb) dka[fb] = dva[fb] = f32x16{};
+  for (int fb = 0; fb < FB; ++fb) dka[fb] = dva[fb] = f32x16{};
 
   // queries before the block's first key see none of its keys (causal)
   const int t0 = p.causal ? k0 / 32 : 0;
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
       split_frag<T>(pr + 8 * kk, phi, plo);
       split_frag<T>(ds + 8 * kk, shi, slo);
 #pragma unroll
-      for (int fb = 0; fb < D / 32; ++fb) {
+      for (int fb = 0; fb < FB; ++fb) {
         const Frag8<T> gb = load_tr_frag<T, D>(gt, fb, kk, lane);
         dva[fb] = mma8(phi, gb, dva[fb]);
         dva[fb] = mma8(plo, gb, dva[fb]);
@@ -434,11 +438,11 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
   T* dv = static_cast<T*>(p.dv) + (int64_t)bh * p.Lk * D;
   bool nonfinite = false;
 #pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb)
+  for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (key < p.Lk) {
+      if (key < p.Lk && 32 * fb + n < D) {
         const T a = (T)(dka[fb][i] * p.scale), b = (T)dva[fb][i];
         dk[(int64_t)key * D + 32 * fb + n] = a;
         dv[(int64_t)key * D + 32 * fb + n] = b;

@@ -53,7 +53,7 @@ def _check(w, what, std=1.0):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("kind", [0, W.CAUSAL, W.PADDING, W.CAUSAL | W.PADDING])
 def test_bwd_parity(dtype, D, kind):
     L = 100 if D == 128 else 130
