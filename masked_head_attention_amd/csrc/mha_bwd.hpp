@@ -185,20 +185,30 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
   return l < 0 ? 0 : (l > p.Lk ? p.Lk : l);
 }
 
-// ---- dQ (and the row statistics) per 32-query block ----------------------
-// TM: a mask tensor (additive or keep) is read; without one the score path
-// has no per-element mask work.
+// ---- dQ (and the row statistics) per group of 4 query blocks --------------
+// Four waves, one 32-query block each, share every K and V tile through LDS:
+// each thread loads its 16-byte pieces of tile t + 1 into registers while the
+// waves work on tile t, and stores them into the other LDS buffer before the
+// tile's barrier. The A operands (K and V rows through keymap) are LDS reads,
+// and dQ's B operand (8 consecutive keys of one feature) is a transposing
+// read of the same row-major K tile.
 template <typename T, int D, bool TM>
-__global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
   // 32-feature blocks of the dQ accumulators (D = 16: one block whose upper
   // 16 columns read the LDS tile's row padding and are never stored)
   constexpr int FB = (D + 31) / 32;
-  __shared__ __attribute__((aligned(16))) char kt[32 * tile_rs<D>()];
-  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
-  int bh = 0, qb = 0;
-  xcd_block(p.B * p.H, p.nqblk, &bh, &qb);
-  if (p.causal) qb = p.nqblk - 1 - qb;  // the longest rows (most key tiles) first
-  const int q0 = qb * 32;
+  constexpr int RS = tile_rs<D>();
+  constexpr int CPR = D / 8;                 // 16-byte pieces per row
+  constexpr int PPT = 32 * CPR;              // pieces per 32-row tile
+  constexpr int PPTH = (PPT + 255) / 256;    // pieces per thread (whole waves idle past PPT)
+  __shared__ __attribute__((aligned(16))) char kv[2][2][32 * RS];  // [buffer][K, V]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int ngrp = (p.nqblk + 3) / 4;
+  int bh = 0, qg = 0;
+  xcd_block(p.B * p.H, ngrp, &bh, &qg);
+  if (p.causal) qg = ngrp - 1 - qg;  // the longest rows (most key tiles) first
+  const int q0 = (4 * qg + wv) * 32;  // this wave's query block
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int qi = q0 + n;  // this lane's query (column of S^T)
@@ -212,43 +222,77 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   Frag8<T> qf[D / 16], gf[D / 16];
   load_rows<T, D>(qrs, qi, hh, qf);
   load_rows<T, D>(grs, qi, hh, gf);
-  // keys past the block's last query are illegal for all its rows (causal)
+  // keys past a block's last query are illegal for all its rows (causal);
+  // the group streams the tiles of its last block, each wave computes its own
   const int kmax = p.causal ? min(kend, q0 + 32) : kend;
-  const int ntile = (kmax + 31) / 32;
+  const int ntile = q0 < p.Lq ? (kmax + 31) / 32 : 0;
+  const int kmax_g = p.causal ? min(kend, 4 * qg * 32 + 128) : kend;
+  const int ntile_g = (kmax_g + 31) / 32;
 
-  // K and V rows of key tile t (through keymap). The tile after the last one
-  // is read at rows past the key range: zeros, no memory traffic.
-  const int tpast = (kend + 31) / 32;
-  auto load_kv = [&](int t, Frag8<T> (&kf)[D / 16], Frag8<T> (&vf)[D / 16]) {
-    const int tt = t < ntile ? t : tpast;
-    load_rows<T, D>(krs, 32 * tt + keymap(n), hh, kf);
-    load_rows<T, D>(vrs, 32 * tt + keymap(n), hh, vf);
+  // staged copy of a K/V tile: piece u = tid + 256 i is row u / CPR, 16-byte
+  // chunk u % CPR; rows past the key range read as zeros
+  uint4 rk[PPTH], rv[PPTH];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < PPTH; ++i) {
+      const int u = tid + 256 * i;
+      if (PPT % 256 == 0 || u < PPT) {
+        const uint32_t off = (uint32_t)(32 * t + u / CPR) * (D * 2) + (u % CPR) * 16;
+        rk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+        rv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+      }
+    }
   };
-  // S^T and dP^T of a tile
-  auto tile = [&](const Frag8<T> (&kf)[D / 16], const Frag8<T> (&vf)[D / 16], f32x16& sa,
-                  f32x16& da) {
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPTH; ++i) {
+      const int u = tid + 256 * i;
+      if (PPT % 256 == 0 || u < PPT) {
+        const int o = (u / CPR) * RS + (u % CPR) * 16;
+        *reinterpret_cast<uint4*>(kv[buf][0] + o) = rk[i];
+        *reinterpret_cast<uint4*>(kv[buf][1] + o) = rv[i];
+      }
+    }
+  };
+  // S^T and dP^T of the tile in buffer buf (K and V rows through keymap)
+  auto tile = [&](int buf, f32x16& sa, f32x16& da) {
+    const char* kr = kv[buf][0] + keymap(n) * RS + 16 * hh;
+    const char* vr = kv[buf][1] + keymap(n) * RS + 16 * hh;
     sa = f32x16{};
     da = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
-      sa = mma8(kf[kb], qf[kb], sa);
-      da = mma8(vf[kb], gf[kb], da);
+      Frag8<T> kf, vf;
+      kf.u[0] = lds_load16(kr + 32 * kb);
+      vf.u[0] = lds_load16(vr + 32 * kb);
+      sa = mma8(kf, qf[kb], sa);
+      da = mma8(vf, gf[kb], da);
     }
   };
   auto legal = [&](int key) { return key < kend && !(p.causal && key > qi); };
+  // one streaming pass over the group's key tiles; body(t, buf) runs for the
+  // tiles of this wave's range
+  auto stream = [&](auto&& body) {
+    if (ntile_g > 0) {
+      gload(0);
+      lstore(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntile_g; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntile_g) gload(t + 1);
+      if (t < ntile) body(t, buf);
+      if (t + 1 < ntile_g) lstore(buf ^ 1);  // last read at tile t - 1, before its barrier
+      __syncthreads();
+    }
+  };
 
   // pass 1: log-sum-exp (log2 units) and Delta = sum_j P_j dP_j of each row:
   // running maximum m, sum l of 2^(s - m) and sum a of 2^(s - m) dP
   float m = -INFINITY, l = 0.f, a = 0.f;
-  Frag8<T> kc[D / 16], vc[D / 16];  // the current tile; the next one is in flight
-  load_kv(0, kc, vc);
-  for (int t = 0; t < ntile; ++t) {
-    Frag8<T> kn[D / 16], vn[D / 16];
-    load_kv(t + 1, kn, vn);
+  stream([&](int t, int buf) {
     f32x16 sa, da;
-    tile(kc, vc, sa, da);
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) { kc[kb] = kn[kb]; vc[kb] = vn[kb]; }
+    tile(buf, sa, da);
     float s[16], mx = m;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -269,7 +313,7 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
       a = __builtin_fmaf(e, da[i], a);
     }
     m = mx;
-  }
+  });
   const float M = pair_max(m);
   const float Mu = (M == -INFINITY) ? 0.f : M;
   const float w = exp2_fast(m - Mu);
@@ -287,20 +331,9 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
   f32x16 dqa[FB];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb) dqa[fb] = f32x16{};
-  load_kv(0, kc, vc);
-  for (int t = 0; t < ntile; ++t) {
-    Frag8<T> kn[D / 16], vn[D / 16];
-    load_kv(t + 1, kn, vn);
+  stream([&](int t, int buf) {
     f32x16 sa, da;
-    tile(kc, vc, sa, da);
-    // The workgroup is this one wave: LDS operations complete in order, so
-    // waiting for this wave's own LDS traffic (not its global loads, which
-    // would drain the prefetch) orders the tile's reads and writes across
-    // lanes; the memory clobber keeps the compiler from moving them.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous tile's reads are done
-    store_rows<T, D>(kt, kc, n, hh);
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) { kc[kb] = kn[kb]; vc[kb] = vn[kb]; }
+    tile(buf, sa, da);
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -315,19 +348,18 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(const BwdParams p) {
       }
       ds[i] = pr * (da[i] - delta);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // kt holds the tile
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       Frag8<T> hi, lo;
       split_frag<T>(ds + 8 * kk, hi, lo);
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        const Frag8<T> kb = load_tr_frag<T, D>(kt, fb, kk, lane);
+        const Frag8<T> kb = load_tr_frag<T, D>(kv[buf][0], fb, kk, lane);
         dqa[fb] = mma8(hi, kb, dqa[fb]);
         dqa[fb] = mma8(lo, kb, dqa[fb]);
       }
     }
-  }
+  });
   // dQ: lane holds feature 32 fb + n of rows 8 (i / 4) + 4 hh + i % 4
   T* dq = static_cast<T*>(p.dq) + (int64_t)bh * p.Lq * D;
   bool nonfinite = false;
@@ -454,10 +486,11 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
 
 template <typename T, int D, bool TM>
 hipError_t launch_bwd_m(const BwdParams& p, hipStream_t stream) {
-  const long long gq = (long long)p.B * p.H * p.nqblk, gk = (long long)p.B * p.H * p.nkblk;
+  const long long gq = (long long)p.B * p.H * ((p.nqblk + 3) / 4);  // groups of 4 query blocks
+  const long long gk = (long long)p.B * p.H * p.nkblk;
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (gq > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(256), 0, stream, p);
   if (gk > 0)
     hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(64), 0, stream, p);
   return hipGetLastError();
