@@ -383,16 +383,27 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-// ---- dK and dV per 32-key block -----------------------------------------
+// ---- dK and dV per group of 4 key blocks -------------------------------------
+// Four waves, one 32-key block each (K and V held in registers), share every
+// query tile through LDS: Q and dO rows and the rows' statistics are staged
+// one tile ahead as in the dq kernel. The A operands (Q and dO rows through
+// keymap) are LDS reads; the B operands of dV += P^T dO and dK += dS^T Q are
+// transposing reads of the same row-major tiles.
 template <typename T, int D, bool TM>
-__global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(const BwdParams p) {
   constexpr int FB = (D + 31) / 32;  // 32-feature blocks of the dK, dV accumulators
-  __shared__ __attribute__((aligned(16))) char qt[32 * tile_rs<D>()];
-  __shared__ __attribute__((aligned(16))) char gt[32 * tile_rs<D>()];
-  const int lane = threadIdx.x, n = lane & 31, hh = lane >> 5;
-  int bh = 0, kb0 = 0;
-  xcd_block(p.B * p.H, p.nkblk, &bh, &kb0);
-  const int k0 = kb0 * 32;
+  constexpr int RS = tile_rs<D>();
+  constexpr int CPR = D / 8;
+  constexpr int PPT = 32 * CPR;
+  constexpr int PPTH = (PPT + 255) / 256;
+  __shared__ __attribute__((aligned(16))) char qg_t[2][2][32 * RS];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float st[2][64];           // [buffer][lse x32, Delta x32]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int ngrp = (p.nkblk + 3) / 4;
+  int bh = 0, kgp = 0;
+  xcd_block(p.B * p.H, ngrp, &bh, &kgp);
+  const int k0 = (4 * kgp + wv) * 32;  // this wave's key block
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int kj = k0 + n;  // this lane's key (column of S)
@@ -412,58 +423,99 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb) dka[fb] = dva[fb] = f32x16{};
 
-  // queries before the block's first key see none of its keys (causal)
+  // queries before a block's first key see none of its keys (causal); a
+  // block past the key length gets zeros. The group streams from its first
+  // block's first query tile; each wave computes from its own.
+  const int k0g = 4 * kgp * 32;
   const int t0 = p.causal ? k0 / 32 : 0;
-  const int ntile = k0 < kend ? (p.Lq + 31) / 32 : 0;  // a padded block gets zeros
-  for (int t = t0; t < ntile; ++t) {
-    Frag8<T> qa[D / 16], ga[D / 16];
-    load_rows<T, D>(qrs, 32 * t + keymap(n), hh, qa);
-    load_rows<T, D>(grs, 32 * t + keymap(n), hh, ga);
-    float lrow[16], drow[16];
+  const int t0g = p.causal ? k0g / 32 : 0;
+  const bool active = k0 < kend;
+  const int ntile = (k0g < kend) ? (p.Lq + 31) / 32 : 0;
+
+  uint4 rq[PPTH], rg[PPTH];
+  float rs = 0.f;  // thread tid < 64: lse (tid < 32) or Delta of row 32 t + tid % 32
+  auto gload = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * t + run_off(i, hh);
-      lrow[i] = row < p.Lq ? lse2[row] : -INFINITY;
-      drow[i] = row < p.Lq ? dlt[row] : 0.f;
-    }
-    f32x16 sa = f32x16{}, da = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      sa = mma8(qa[kb], kf[kb], sa);
-      da = mma8(ga[kb], vf[kb], da);
-    }
-    __syncthreads();  // the previous tile's reads of qt, gt are done
-    store_rows<T, D>(qt, qa, n, hh);
-    store_rows<T, D>(gt, ga, n, hh);
-    float pr[16], ds[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * t + run_off(i, hh);
-      const bool ok = kj < kend && !(p.causal && kj > row) && lrow[i] != -INFINITY;
-      if constexpr (TM) {
-        const float x = ok ? masked_logit(p, sa[i] * p.c, mask_at<T>(p, bh, row, kj)) : -INFINITY;
-        pr[i] = x != -INFINITY ? exp2_fast(x - lrow[i]) : 0.f;
-      } else {
-        pr[i] = ok ? exp2_fast(sa[i] * p.c - lrow[i]) : 0.f;
-      }
-      ds[i] = pr[i] * (da[i] - drow[i]);
-    }
-    __syncthreads();  // qt, gt hold the tile
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      Frag8<T> phi, plo, shi, slo;
-      split_frag<T>(pr + 8 * kk, phi, plo);
-      split_frag<T>(ds + 8 * kk, shi, slo);
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb) {
-        const Frag8<T> gb = load_tr_frag<T, D>(gt, fb, kk, lane);
-        dva[fb] = mma8(phi, gb, dva[fb]);
-        dva[fb] = mma8(plo, gb, dva[fb]);
-        const Frag8<T> qb = load_tr_frag<T, D>(qt, fb, kk, lane);
-        dka[fb] = mma8(shi, qb, dka[fb]);
-        dka[fb] = mma8(slo, qb, dka[fb]);
+    for (int i = 0; i < PPTH; ++i) {
+      const int u = tid + 256 * i;
+      if (PPT % 256 == 0 || u < PPT) {
+        const uint32_t off = (uint32_t)(32 * t + u / CPR) * (D * 2) + (u % CPR) * 16;
+        rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+        rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
       }
     }
+    if (tid < 64) {  // rows past Lq: no weight (-inf) and no Delta
+      const int row = 32 * t + (tid & 31);
+      rs = tid < 32 ? (row < p.Lq ? lse2[row] : -INFINITY) : (row < p.Lq ? dlt[row] : 0.f);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPTH; ++i) {
+      const int u = tid + 256 * i;
+      if (PPT % 256 == 0 || u < PPT) {
+        const int o = (u / CPR) * RS + (u % CPR) * 16;
+        *reinterpret_cast<uint4*>(qg_t[buf][0] + o) = rq[i];
+        *reinterpret_cast<uint4*>(qg_t[buf][1] + o) = rg[i];
+      }
+    }
+    if (tid < 64) st[buf][tid] = rs;
+  };
+
+  if (ntile > t0g) {
+    gload(t0g);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int t = t0g; t < ntile; ++t) {
+    const int buf = (t - t0g) & 1;
+    if (t + 1 < ntile) gload(t + 1);
+    if (active && t >= t0) {
+      // S = Q K^T and dP = dO V^T (Q and dO rows through keymap)
+      const char* qr = qg_t[buf][0] + keymap(n) * RS + 16 * hh;
+      const char* gr = qg_t[buf][1] + keymap(n) * RS + 16 * hh;
+      f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        Frag8<T> qa, ga;
+        qa.u[0] = lds_load16(qr + 32 * kb);
+        ga.u[0] = lds_load16(gr + 32 * kb);
+        sa = mma8(qa, kf[kb], sa);
+        da = mma8(ga, vf[kb], da);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * t + run_off(i, hh);
+        const float lrow = st[buf][run_off(i, hh)], drow = st[buf][32 + run_off(i, hh)];
+        const bool ok = kj < kend && !(p.causal && kj > row) && lrow != -INFINITY;
+        if constexpr (TM) {
+          const float x =
+              ok ? masked_logit(p, sa[i] * p.c, mask_at<T>(p, bh, row, kj)) : -INFINITY;
+          pr[i] = x != -INFINITY ? exp2_fast(x - lrow) : 0.f;
+        } else {
+          pr[i] = ok ? exp2_fast(sa[i] * p.c - lrow) : 0.f;
+        }
+        ds[i] = pr[i] * (da[i] - drow);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        Frag8<T> phi, plo, shi, slo;
+        split_frag<T>(pr + 8 * kk, phi, plo);
+        split_frag<T>(ds + 8 * kk, shi, slo);
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+          const Frag8<T> gb = load_tr_frag<T, D>(qg_t[buf][1], fb, kk, lane);
+          dva[fb] = mma8(phi, gb, dva[fb]);
+          dva[fb] = mma8(plo, gb, dva[fb]);
+          const Frag8<T> qb = load_tr_frag<T, D>(qg_t[buf][0], fb, kk, lane);
+          dka[fb] = mma8(shi, qb, dka[fb]);
+          dka[fb] = mma8(slo, qb, dka[fb]);
+        }
+      }
+    }
+    if (t + 1 < ntile) lstore(buf ^ 1);  // last read at tile t - 1, before its barrier
+    __syncthreads();
   }
   // lane holds feature 32 fb + n of keys 8 (i / 4) + 4 hh + i % 4
   T* dk = static_cast<T*>(p.dk) + (int64_t)bh * p.Lk * D;
@@ -487,12 +539,12 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(const BwdParams p) {
 template <typename T, int D, bool TM>
 hipError_t launch_bwd_m(const BwdParams& p, hipStream_t stream) {
   const long long gq = (long long)p.B * p.H * ((p.nqblk + 3) / 4);  // groups of 4 query blocks
-  const long long gk = (long long)p.B * p.H * p.nkblk;
+  const long long gk = (long long)p.B * p.H * ((p.nkblk + 3) / 4);  // groups of 4 key blocks
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (gq > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(256), 0, stream, p);
   if (gk > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
