@@ -392,8 +392,13 @@ bwd_dq_kernel(const BwdParams p) {
 // one tile ahead as in the dq kernel. The A operands (Q and dO rows through
 // keymap) are LDS reads; the B operands of dV += P^T dO and dK += dS^T Q are
 // transposing reads of the same row-major tiles.
+// Two workgroups per CU (at most 256 registers per lane). The V operand is
+// reloaded from L2 for every tile (its latency hides behind the S MFMAs) so
+// that K, both accumulators and the tile's values fit: at D = 128, 6 spilled
+// registers instead of 37.
 template <typename T, int D, bool TM>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_dkv_kernel(const BwdParams p) {
   constexpr int FB = (D + 31) / 32;  // 32-feature blocks of the dK, dV accumulators
   constexpr int RS = tile_rs<D>();
   constexpr int CPR = D / 8;
@@ -419,9 +424,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const BwdParams p) {
   const float* lse2 = p.lse2 + (int64_t)bh * p.Lq;
   const float* dlt = p.delta + (int64_t)bh * p.Lq;
 
-  Frag8<T> kf[D / 16], vf[D / 16];
+  Frag8<T> kf[D / 16];
   load_rows<T, D>(krs, kj, hh, kf);
-  load_rows<T, D>(vrs, kj, hh, vf);
   f32x16 dka[FB], dva[FB];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb) dka[fb] = dva[fb] = f32x16{};
@@ -474,6 +478,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const BwdParams p) {
     const int buf = (t - t0g) & 1;
     if (t + 1 < ntile) gload(t + 1);
     if (active && t >= t0) {
+      Frag8<T> vf[D / 16];  // V rows reloaded from L2 per tile (frees their registers)
+      load_rows<T, D>(vrs, kj, hh, vf);
       // S = Q K^T and dP = dO V^T (Q and dO rows through keymap)
       const char* qr = qg_t[buf][0] + keymap(n) * RS + 16 * hh;
       const char* gr = qg_t[buf][1] + keymap(n) * RS + 16 * hh;
