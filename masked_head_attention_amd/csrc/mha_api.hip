@@ -217,7 +217,7 @@ mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout
   if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
   if (B == 0 || H == 0 || (Lq == 0 && Lk == 0)) return MHA_OK;  // empty call
   if (ptr_kinds && !mask) return MHA_E_NULL;
-  if (!dk || !dv || (Lk > 0 && (!k || !v))) return MHA_E_NULL;
+  if (Lk > 0 && (!k || !v || !dk || !dv)) return MHA_E_NULL;
   if (Lq > 0 && (!q || !dout || !dq)) return MHA_E_NULL;
   const void* ptrs16[] = {q, k, v, dout, dq, dk, dv};
   for (const void* p : ptrs16)

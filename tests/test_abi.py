@@ -241,6 +241,7 @@ def _bwd(q=A, k=A, v=A, dout=A, mask=None, kind=0, B=1, H=2, Lq=8, Lk=8, D=64, s
     (dict(Lk=1 << 24, D=128), "MHA_E_OVERFLOW"),
     (dict(B=0), "MHA_OK"),
     (dict(Lq=0, Lk=0), "MHA_OK"),
+    (dict(Lk=0, k=None, v=None, dk=None, dv=None, ws=None, ws_bytes=0), "MHA_E_WORKSPACE"),
 ])
 def test_bwd_validation(kw, status):
     assert _bwd(**kw) == status

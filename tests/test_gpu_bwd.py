@@ -110,3 +110,21 @@ def test_bwd_workload_full_size_sampled():
             assert_parity(a, b, w.dtype, f"bwd-workload head {h} {name}")
     assert np.isfinite(gq).all() and np.isfinite(gk).all() and np.isfinite(gv).all()
     del torch
+
+
+def test_bwd_empty_key_or_query_ranges():
+    """Lk = 0: every row is fully masked, dq = 0 and the flag is raised.
+    Lq = 0: no query reaches any key, dk = dv = 0."""
+    import masked_head_attention_amd as M
+    import torch
+
+    q = torch.randn(2, 3, 40, 64, device="cuda").half()
+    z = torch.zeros(2, 3, 0, 64, dtype=torch.float16, device="cuda")
+    dq, dk, dv = M.bwd(q, z, z, torch.randn_like(q))
+    assert M.get_flags(clear=True) == M.FLAG_FULLY_MASKED_ROW
+    assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
+    k = torch.randn(2, 3, 50, 64, device="cuda").half()
+    e = torch.zeros(2, 3, 0, 64, dtype=torch.float16, device="cuda")
+    dq, dk, dv = M.bwd(e, k, k.clone(), e, kind=M.CAUSAL)
+    assert M.get_flags(clear=True) == 0
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
