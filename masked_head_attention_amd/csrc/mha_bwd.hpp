@@ -388,15 +388,15 @@ bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---- dK and dV per group of 4 key blocks -------------------------------------
-// Four waves, one 32-key block each (K and V held in registers), share every
+// Four waves, one 32-key block each (K in registers, V in LDS), share every
 // query tile through LDS: Q and dO rows and the rows' statistics are staged
 // one tile ahead as in the dq kernel. The A operands (Q and dO rows through
 // keymap) are LDS reads; the B operands of dV += P^T dO and dK += dS^T Q are
 // transposing reads of the same row-major tiles.
-// Two workgroups per CU (at most 256 registers per lane). The V operand is
-// reloaded from L2 for every tile (its latency hides behind the S MFMAs) so
-// that K, both accumulators and the tile's values fit: at D = 128, 6 spilled
-// registers instead of 37.
+// Two workgroups per CU (at most 256 registers per lane, 78 KB of LDS each at
+// D = 128). The V operand lives in the wave's own LDS tile rather than in
+// registers, so that K, both accumulators and the tile's values fit: 6
+// spilled registers at D = 128 instead of 37.
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dkv_kernel(const BwdParams p) {
@@ -407,6 +407,7 @@ bwd_dkv_kernel(const BwdParams p) {
   constexpr int PPTH = (PPT + 255) / 256;
   __shared__ __attribute__((aligned(16))) char qg_t[2][2][32 * RS];  // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float st[2][64];           // [buffer][lse x32, Delta x32]
+  __shared__ __attribute__((aligned(16))) char vt[4][32 * RS];       // each wave's V rows
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int ngrp = (p.nkblk + 3) / 4;
@@ -427,6 +428,15 @@ bwd_dkv_kernel(const BwdParams p) {
 
   Frag8<T> kf[D / 16];
   load_rows<T, D>(krs, kj, hh, kf);
+  {
+    // this wave's V rows, row-major in its own LDS tile (read back by its own
+    // lanes after the barrier that precedes the tile loop)
+    Frag8<T> v0[D / 16];
+    load_rows<T, D>(vrs, kj, hh, v0);
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+      *reinterpret_cast<uint4*>(vt[wv] + n * RS + (16 * kb + 8 * hh) * 2) = v0[kb].u[0];
+  }
   f32x16 dka[FB], dva[FB];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb) dka[fb] = dva[fb] = f32x16{};
@@ -479,8 +489,6 @@ bwd_dkv_kernel(const BwdParams p) {
     const int buf = (t - t0g) & 1;
     if (t + 1 < ntile) gload(t + 1);
     if (active && t >= t0) {
-      Frag8<T> vf[D / 16];  // V rows reloaded from L2 per tile (frees their registers)
-      load_rows<T, D>(vrs, kj, hh, vf);
       // S = Q K^T and dP = dO V^T (Q and dO rows through keymap)
       const char* qr = qg_t[buf][0] + keymap(n) * RS + 16 * hh;
       const char* gr = qg_t[buf][1] + keymap(n) * RS + 16 * hh;
@@ -488,10 +496,12 @@ bwd_dkv_kernel(const BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
         Frag8<T> qa, ga;
+        Frag8<T> vb;
         qa.u[0] = lds_load16(qr + 32 * kb);
         ga.u[0] = lds_load16(gr + 32 * kb);
+        vb.u[0] = lds_load16(vt[wv] + n * RS + (16 * kb + 8 * hh) * 2);
         sa = mma8(qa, kf[kb], sa);
-        da = mma8(ga, vf[kb], da);
+        da = mma8(ga, vb, da);
       }
       float pr[16], ds[16];
 #pragma unroll
