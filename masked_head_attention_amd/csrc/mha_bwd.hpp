@@ -88,16 +88,6 @@ __device__ inline void split_frag(const float* x, Frag8<T>& hi, Frag8<T>& lo) {
 template <int D>
 constexpr int tile_rs() { return D * 2 + 48; }
 
-// Writes a lane's 16-byte pieces of a 32-row tile (row keymap(l % 32),
-// features 16 kb + 8 hh .. +7) into the LDS tile.
-template <typename T, int D>
-__device__ inline void store_rows(char* t, const Frag8<T> (&f)[D / 16], int n, int hh) {
-  char* r = t + keymap(n) * tile_rs<D>();
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb)
-    *reinterpret_cast<uint4*>(r + (16 * kb + 8 * hh) * 2) = f[kb].u[0];
-}
-
 typedef __fp16 bwd_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __bf16 bwd_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 template <typename T>
