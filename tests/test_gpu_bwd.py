@@ -128,3 +128,17 @@ def test_bwd_empty_key_or_query_ranges():
     dq, dk, dv = M.bwd(e, k, k.clone(), e, kind=M.CAUSAL)
     assert M.get_flags(clear=True) == 0
     assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_bwd_noncausal_long_rows_sampled():
+    """No mask, bfloat16, L = 1024, D = 128: two heads against the oracle."""
+    w = W.make("bwd-long", "bf16", 1, 4, 1024, 1024, 128, seed=61)
+    g = W.grad_output(w)
+    gq, gk, gv, flags = _run(w, g)
+    assert flags == 0
+    for h in (0, 3):
+        sl = slice(h, h + 1)
+        rq, rk, rv, _ = oracle.mha_bwd(w.f64("q")[:, sl], w.f64("k")[:, sl], w.f64("v")[:, sl],
+                                       W.to_f64(g, w.dtype)[:, sl], 0, None, None, w.scale)
+        for name, a, b in [("dq", gq[:, sl], rq), ("dk", gk[:, sl], rk), ("dv", gv[:, sl], rv)]:
+            assert_parity(a, b, w.dtype, f"bwd-long head {h} {name}")

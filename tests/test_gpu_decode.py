@@ -183,3 +183,16 @@ def test_decode_workload_full_size_sampled():
     assert_parity(got[bs, hs], ref[:, 0], w.dtype, "decode-workload-sampled")
     assert np.all(np.abs(glse[bs, hs] - rlse[:, 0]) <= lse_tol(rlse[:, 0]))
     assert np.isfinite(got).all() and np.isfinite(glse).all()
+
+
+def test_decode_very_long_cache():
+    """A 65536-key cache: 1024 splits per head, so the merge walks 16 groups
+    of 64 splits; lengths cover one split, a group boundary and the full cache."""
+    import masked_head_attention_amd as M
+
+    B, H, Lk, D = 3, 2, 65536, 128
+    need = M.decode_workspace_size(B, H, Lk, D, M.BF16)
+    assert need // (B * H * (D + 2) * 4) == Lk // 64
+    w = _work("bf16", B, H, Lk, D, seed=60, lens_range=(1, Lk))
+    lens = np.array([37, 64 * 64 + 5, Lk], np.int32)
+    _check(w, "decode-long-cache", lens=lens)
