@@ -469,6 +469,9 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
+      // both MFMA blocks run at raised wave priority: the SIMD's other wave
+      // then fills the matrix core's gaps with its softmax arithmetic
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
@@ -477,6 +480,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
           s[blk] = mma8(kf, qf[cc], s[blk]);
         }
+      __builtin_amdgcn_s_setprio(0);
       // online softmax over the tile [MAX 2.3]. ADD: s becomes the logit
       // scale*s + mask (natural units); otherwise s stays raw (scale > 0
       // commutes with the max) and the scale is applied in the exponent's FMA
@@ -538,6 +542,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           if constexpr (!SUM_PACKED) rs += e;
         }
       // O^T += V^T P^T, 16 keys per MFMA k-step
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
@@ -585,6 +590,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
             }
           }
         }
+      __builtin_amdgcn_s_setprio(0);
       l_run += rs;
     };
 
