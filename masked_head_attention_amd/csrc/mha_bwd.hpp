@@ -184,9 +184,7 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
 // and dQ's B operand (8 consecutive keys of one feature) is a transposing
 // read of the same row-major K tile.
 // Two workgroups per CU (at most 256 registers per lane): at D = 128 the
-// compiler fits it in 220 without spills, against 284 when left to itself.
-// The MFMA blocks of both kernels run at raised wave priority, so the other
-// wave on the SIMD fills the matrix core's gaps with its vector work.
+// compiler fits it in 243 without spills, against 284 when left to itself.
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dq_kernel(const BwdParams p) {
@@ -254,7 +252,6 @@ bwd_dq_kernel(const BwdParams p) {
   auto tile = [&](int buf, f32x16& sa, f32x16& da) {
     const char* kr = kv[buf][0] + keymap(n) * RS + 16 * hh;
     const char* vr = kv[buf][1] + keymap(n) * RS + 16 * hh;
-    __builtin_amdgcn_s_setprio(1);
     sa = f32x16{};
     da = f32x16{};
 #pragma unroll
@@ -265,7 +262,6 @@ bwd_dq_kernel(const BwdParams p) {
       sa = mma8(kf, qf[kb], sa);
       da = mma8(vf, gf[kb], da);
     }
-    __builtin_amdgcn_s_setprio(0);
   };
   auto legal = [&](int key) { return key < kend && !(p.causal && key > qi); };
   // one streaming pass over the group's key tiles; body(t, buf) runs for the
@@ -346,7 +342,6 @@ bwd_dq_kernel(const BwdParams p) {
       }
       ds[i] = pr * (da[i] - delta);
     }
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       Frag8<T> hi, lo;
@@ -358,7 +353,6 @@ bwd_dq_kernel(const BwdParams p) {
         dqa[fb] = mma8(lo, kb, dqa[fb]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
   });
   // dQ: lane holds feature 32 fb + n of rows 8 (i / 4) + 4 hh + i % 4
   T* dq = static_cast<T*>(p.dq) + (int64_t)bh * p.Lq * D;
@@ -393,6 +387,8 @@ bwd_dq_kernel(const BwdParams p) {
 // D = 128). The V operand lives in the wave's own LDS tile rather than in
 // registers, so that K, both accumulators and the tile's values fit: 2
 // spilled registers at D = 128 instead of 37.
+// The MFMA blocks run at raised wave priority, so the SIMD's other wave fills
+// the matrix core's gaps with its vector work (in the dq kernel this lost).
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dkv_kernel(const BwdParams p) {
