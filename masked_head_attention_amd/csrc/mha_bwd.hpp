@@ -185,6 +185,9 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
 // read of the same row-major K tile.
 // Two workgroups per CU (at most 256 registers per lane): at D = 128 the
 // compiler fits it in 243 without spills, against 284 when left to itself.
+// The dQ product runs at raised wave priority, so the SIMD's other wave fills
+// the matrix core's gaps with its vector work (around the S and dP products,
+// which both passes share, this lost).
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dq_kernel(const BwdParams p) {
@@ -342,6 +345,7 @@ bwd_dq_kernel(const BwdParams p) {
       }
       ds[i] = pr * (da[i] - delta);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       Frag8<T> hi, lo;
@@ -353,6 +357,7 @@ bwd_dq_kernel(const BwdParams p) {
         dqa[fb] = mma8(lo, kb, dqa[fb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   });
   // dQ: lane holds feature 32 fb + n of rows 8 (i / 4) + 4 hh + i % 4
   T* dq = static_cast<T*>(p.dq) + (int64_t)bh * p.Lq * D;
@@ -387,8 +392,7 @@ bwd_dq_kernel(const BwdParams p) {
 // D = 128). The V operand lives in the wave's own LDS tile rather than in
 // registers, so that K, both accumulators and the tile's values fit: 2
 // spilled registers at D = 128 instead of 37.
-// The MFMA blocks run at raised wave priority, so the SIMD's other wave fills
-// the matrix core's gaps with its vector work (in the dq kernel this lost).
+// Both MFMA blocks run at raised wave priority, as the dq kernel's dQ product.
 template <typename T, int D, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dkv_kernel(const BwdParams p) {
