@@ -130,17 +130,25 @@ __device__ inline void load_rows(const __amdgpu_buffer_rsrc_t rs, int row, int h
                    rs, (uint32_t)row * (D * 2) + (16 * kb + 8 * hh) * 2, 0, 0));
 }
 
-// Workgroup -> (head, 32-row block). Workgroups are dealt to the 8 XCDs
+// Workgroup -> (head, block group). Workgroups are dealt to the 8 XCDs
 // round-robin; this map keeps every block of a head on one XCD, so the tiles
 // that all blocks of the head stream (K and V, or Q and dO) stay in that
 // XCD's L2. Heads beyond the last complete group of 8 keep the plain order.
+// An XCD's 32 CUs take its workgroups in turn, so with two per CU its
+// workgroups j and j + 32 share one; under a causal mask the work of a block
+// group grows (dq) or shrinks (dkv) with its index. A head group whose first
+// workgroup falls in an odd 32-workgroup run takes its blocks in reverse
+// order, so that a CU holding a long group also holds a short one. The order
+// is chosen per head group, so the map stays one-to-one for every shape.
 __device__ inline void xcd_block(int nbh, int nblk, int* bh, int* blk) {
   const int i = blockIdx.x;
   const int full = (nbh / 8) * 8 * nblk;
   if (i < full) {
     const int x = i % 8, j = i / 8;
-    *bh = (j / nblk) * 8 + x;
+    const int hg = j / nblk;
+    *bh = hg * 8 + x;
     *blk = j % nblk;
+    if ((hg * nblk / 32) & 1) *blk = nblk - 1 - *blk;
   } else {
     *bh = i / nblk;
     *blk = i - *bh * nblk;
