@@ -142,3 +142,41 @@ def test_bwd_noncausal_long_rows_sampled():
                                        W.to_f64(g, w.dtype)[:, sl], 0, None, None, w.scale)
         for name, a, b in [("dq", gq[:, sl], rq), ("dk", gk[:, sl], rk), ("dv", gv[:, sl], rv)]:
             assert_parity(a, b, w.dtype, f"bwd-long head {h} {name}")
+
+
+@pytest.mark.parametrize("B,H,L", [(3, 15, 1024), (1, 40, 2048)])
+def test_bwd_block_map_covers_every_block(B, H, L):
+    """Both kernels map workgroups to (head, block group) with the order of
+    some head groups reversed (so that long and short causal groups share a
+    CU) and the heads past the last group of 8 in plain order. Each block's
+    gradients do not depend on which workgroup computes them, so the whole
+    call must equal one call per head bit for bit: a block computed twice or
+    never would not. One head of a reversed group is also checked against the
+    oracle."""
+    import masked_head_attention_amd as M
+    import torch
+
+    w = W.make("bwd-map", "f16", B, H, L, L, 64, kind=W.CAUSAL | W.PADDING, seed=71,
+               lens_range=(300, L))
+    g = W.grad_output(w)
+    gq, gk, gv, flags = _run(w, g)
+    assert flags == 0
+    q, k, v, go = (to_dev(a, w.dtype) for a in (w.q, w.k, w.v, g))
+    lens = to_dev(w.lens, w.dtype)
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            one = M.bwd(*(t[sl].contiguous() for t in (q, k, v)), go[sl].contiguous(),
+                        mask=lens[b:b + 1].contiguous(), kind=w.kind, scale=w.scale)
+            for name, whole, part in zip(("dq", "dk", "dv"), (gq, gk, gv), one):
+                assert np.array_equal(whole[sl], from_dev(part)), (b, h, name)
+    assert M.get_flags(clear=True) == 0
+    bh = 33  # head group 4: reversed in the first shape, not in the second
+    b, h = divmod(bh, H)
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    rq, rk, rv, _ = oracle.mha_bwd(w.f64("q")[sl], w.f64("k")[sl], w.f64("v")[sl],
+                                   W.to_f64(g, w.dtype)[sl], w.kind, w.lens[b:b + 1], None,
+                                   w.scale)
+    for name, a, r in [("dq", gq[sl], rq), ("dk", gk[sl], rk), ("dv", gv[sl], rv)]:
+        assert_parity(a, r, w.dtype, f"bwd-map head {bh} {name}")
+    del torch
