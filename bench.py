@@ -118,7 +118,7 @@ KERNEL_SOURCES = {
                   "mha_inst_bf16.hip", "mha_inst_f16.hip", "mha_inst_f32.hip"),
     SOFTMAX_KERNEL_NAME: ("mha_common.hpp", "mha_softmax.hpp", "mha_softmax.hip"),
     DECODE_KERNEL_NAME: ("mha_common.hpp", "mha_decode.hpp", "mha_decode.hip"),
-    BWD_KERNEL_NAME: ("mha_common.hpp", "mha_bwd.hpp", "mha_bwd.hip"),
+    BWD_KERNEL_NAME: ("mha_common.hpp", "mha_bwd.hpp", "mha_bwd_f32.hpp", "mha_bwd.hip"),
 }
 
 

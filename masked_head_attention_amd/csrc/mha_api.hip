@@ -213,7 +213,6 @@ mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout
   if (!ptr_kinds && mask) return MHA_E_MASK;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return MHA_E_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
-  if (dtype == MHA_F32) return MHA_E_UNSUPPORTED;
   if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
   if (B == 0 || H == 0 || (Lq == 0 && Lk == 0)) return MHA_OK;  // empty call
   if (ptr_kinds && !mask) return MHA_E_NULL;

@@ -222,7 +222,7 @@ def _bwd(q=A, k=A, v=A, dout=A, mask=None, kind=0, B=1, H=2, Lq=8, Lk=8, D=64, s
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=5), "MHA_E_DTYPE"),
-    (dict(dtype=0), "MHA_E_UNSUPPORTED"),
+    (dict(dtype=0, D=48), "MHA_E_UNSUPPORTED"),
     (dict(D=48), "MHA_E_UNSUPPORTED"),
     (dict(kind=_abi.ADDITIVE | _abi.PADDING, mask=A), "MHA_E_MASK"),
     (dict(kind=_abi.PER_HEAD), "MHA_E_MASK"),

@@ -3,8 +3,8 @@ attention forward for an upstream gradient dO, through the softmax Jacobian of
 "Why attention must compute the max first", section 3.3) against the fp64
 oracle, through the C ABI.
 
-Bar: |gpu - oracle| <= 2e-3 + half an output ulp elementwise for every
-gradient (float16 / bfloat16); flags agree exactly.
+Bar: |gpu - oracle| <= 2e-3 (float16 / bfloat16) or 1e-5 (float32) + half an
+output ulp elementwise for every gradient; flags agree exactly.
 """
 import numpy as np
 import pytest
@@ -52,7 +52,7 @@ def _check(w, what, std=1.0):
     assert flags == rflags, (what, flags, rflags)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("kind", [0, W.CAUSAL, W.PADDING, W.CAUSAL | W.PADDING])
 def test_bwd_parity(dtype, D, kind):
@@ -63,7 +63,7 @@ def test_bwd_parity(dtype, D, kind):
     _check(w, f"bwd-{dtype}-D{D}-kind{kind}")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("kind", [W.ADDITIVE, W.ADDITIVE | W.CAUSAL, W.KEEP,
                                   W.ADDITIVE | W.PER_HEAD, W.KEEP | W.PER_HEAD | W.CAUSAL])
 def test_bwd_tensor_masks(dtype, kind):
@@ -74,17 +74,19 @@ def test_bwd_tensor_masks(dtype, kind):
     _check(w, f"bwd-mask-{dtype}-{kind}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("Lq,Lk", [(1, 1), (33, 70), (70, 33), (64, 64), (5, 200)])
-def test_bwd_shapes(Lq, Lk):
-    w = W.make("bwd-shapes", "f16", 1, 2, Lq, Lk, 64, seed=Lq * 7 + Lk, qkv_std=1.5)
-    _check(w, f"bwd-shape-{Lq}x{Lk}")
+def test_bwd_shapes(dtype, Lq, Lk):
+    w = W.make("bwd-shapes", dtype, 1, 2, Lq, Lk, 64, seed=Lq * 7 + Lk, qkv_std=1.5)
+    _check(w, f"bwd-shape-{dtype}-{Lq}x{Lk}")
 
 
-def test_bwd_zero_lengths_and_flags():
-    w = W.make("bwd-len0", "bf16", 3, 2, 40, 40, 64, kind=W.PADDING | W.CAUSAL, seed=31,
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_zero_lengths_and_flags(dtype):
+    w = W.make("bwd-len0", dtype, 3, 2, 40, 40, 64, kind=W.PADDING | W.CAUSAL, seed=31,
                lens_range=(0, 40))
     w.lens = np.array([0, 40, 17], np.int32)
-    _check(w, "bwd-len0")
+    _check(w, f"bwd-len0-{dtype}")
 
 
 def test_bwd_large_gradients():
@@ -112,19 +114,21 @@ def test_bwd_workload_full_size_sampled():
     del torch
 
 
-def test_bwd_empty_key_or_query_ranges():
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_bwd_empty_key_or_query_ranges(dtype):
     """Lk = 0: every row is fully masked, dq = 0 and the flag is raised.
     Lq = 0: no query reaches any key, dk = dv = 0."""
     import masked_head_attention_amd as M
     import torch
 
-    q = torch.randn(2, 3, 40, 64, device="cuda").half()
-    z = torch.zeros(2, 3, 0, 64, dtype=torch.float16, device="cuda")
+    td = torch.float16 if dtype == "f16" else torch.float32
+    q = torch.randn(2, 3, 40, 64, device="cuda").to(td)
+    z = torch.zeros(2, 3, 0, 64, dtype=td, device="cuda")
     dq, dk, dv = M.bwd(q, z, z, torch.randn_like(q))
     assert M.get_flags(clear=True) == M.FLAG_FULLY_MASKED_ROW
     assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
-    k = torch.randn(2, 3, 50, 64, device="cuda").half()
-    e = torch.zeros(2, 3, 0, 64, dtype=torch.float16, device="cuda")
+    k = torch.randn(2, 3, 50, 64, device="cuda").to(td)
+    e = torch.zeros(2, 3, 0, 64, dtype=td, device="cuda")
     dq, dk, dv = M.bwd(e, k, k.clone(), e, kind=M.CAUSAL)
     assert M.get_flags(clear=True) == 0
     assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
