@@ -184,3 +184,11 @@ def test_bwd_block_map_covers_every_block(B, H, L):
     for name, a, r in [("dq", gq[sl], rq), ("dk", gk[sl], rk), ("dv", gv[sl], rv)]:
         assert_parity(a, r, w.dtype, f"bwd-map head {bh} {name}")
     del torch
+
+
+def test_bwd_f32_long_ragged_rows():
+    """float32 at L = 517 (eight full 64-key chunks and a ragged one), D = 128,
+    causal with padding lengths, against the oracle everywhere."""
+    w = W.make("bwd-f32-long", "f32", 1, 2, 517, 517, 128, kind=W.CAUSAL | W.PADDING, seed=81,
+               lens_range=(200, 517))
+    _check(w, "bwd-f32-long")
