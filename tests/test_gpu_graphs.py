@@ -68,15 +68,17 @@ def test_decode_graph_replays():
     assert M.get_flags(clear=True) == 0
 
 
-def test_backward_graph_replays():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_graph_replays(dtype):
     import masked_head_attention_amd as M
     import torch
 
-    w = W.make("graph-bwd", "bf16", 1, 4, 200, 200, 64, kind=W.CAUSAL, seed=51)
+    w = W.make("graph-bwd", dtype, 1, 4, 200, 200, 64, kind=W.CAUSAL, seed=51)
     q, k, v = (to_dev(getattr(w, n), w.dtype) for n in ("q", "k", "v"))
     g = to_dev(W.grad_output(w), w.dtype)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(M.bwd_workspace_size(w.B, w.H, w.Lq, M.BF16), dtype=torch.uint8,
+    code = M.BF16 if dtype == "bf16" else M.F32
+    ws = torch.empty(M.bwd_workspace_size(w.B, w.H, w.Lq, code), dtype=torch.uint8,
                      device="cuda")
     _replays(lambda: M.bwd(q, k, v, g, kind=w.kind, scale=w.scale, dq=dq, dk=dk, dv=dv,
                            workspace=ws), [dq, dk, dv])
