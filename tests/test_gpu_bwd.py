@@ -89,6 +89,17 @@ def test_bwd_zero_lengths_and_flags(dtype):
     _check(w, f"bwd-len0-{dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_bwd_out_of_range_lengths(dtype):
+    """Lengths below 0 or above Lk act clamped (no key; every key) and raise
+    the bad-length flag, as in the forward; the clamped-to-0 rows are fully
+    masked."""
+    w = W.make("bwd-badlen", dtype, 3, 2, 40, 40, 64, kind=W.PADDING, seed=33,
+               lens_range=(1, 40))
+    w.lens = np.array([-3, 57, 17], np.int32)
+    _check(w, f"bwd-badlen-{dtype}")
+
+
 def test_bwd_large_gradients():
     w = W.make("bwd-large", "f16", 1, 4, 96, 96, 64, kind=W.CAUSAL, seed=32, qkv_std=2.0)
     _check(w, "bwd-large", std=4.0)
