@@ -317,39 +317,64 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p)
   const float* ml = p.part_ml + bh * p.nsplit * 2;
   const float* po = p.part_o + bh * p.nsplit * D;
   // split s's (m, l) is read by lane s % 64; maxima and sums are wave reductions
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-  for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, O[FPL];
+  float M = -INFINITY, L = 0.f, O[FPL];
 #pragma unroll
   for (int r = 0; r < FPL; ++r) O[r] = 0.f;
-  constexpr int SB = 8;  // splits whose partial outputs are loaded together
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int n = min(64, ns - s0);
-    float w = 0.f;  // weight of split s0 + lane
-    if (lane < n) {
-      const float2 v = *reinterpret_cast<const float2*>(ml + 2 * (s0 + lane));
-      w = exp2_fast(v.x - Mu);
-      L = __builtin_fmaf(v.y, w, L);
+  constexpr int NH = 32;  // up to NH splits: every load of the head issued at once
+  if (ns <= NH) {
+    float2 v = make_float2(-INFINITY, 0.f);
+    if (lane < ns) v = *reinterpret_cast<const float2*>(ml + 2 * lane);
+    float x[NH][FPL];
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int r = 0; r < FPL; ++r) {
+        const int f = lane + 64 * r;
+        x[j][r] = (j < ns && f < D) ? po[(int64_t)j * D + f] : 0.f;
+      }
+    M = v.x;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float w = (lane < ns) ? exp2_fast(v.x - Mu) : 0.f;  // weight of split `lane`
+    L = v.y * w;
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+#pragma unroll
+      for (int r = 0; r < FPL; ++r) O[r] = __builtin_fmaf(x[j][r], wj, O[r]);
     }
-    for (int j0 = 0; j0 < n; j0 += SB) {
-      float x[SB][FPL];
+  } else {
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
-      for (int j = 0; j < SB; ++j)
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    constexpr int SB = 8;  // splits whose partial outputs are loaded together
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int n = min(64, ns - s0);
+      float w = 0.f;  // weight of split s0 + lane
+      if (lane < n) {
+        const float2 v = *reinterpret_cast<const float2*>(ml + 2 * (s0 + lane));
+        w = exp2_fast(v.x - Mu);
+        L = __builtin_fmaf(v.y, w, L);
+      }
+      for (int j0 = 0; j0 < n; j0 += SB) {
+        float x[SB][FPL];
 #pragma unroll
-        for (int r = 0; r < FPL; ++r) {
-          const int f = lane + 64 * r;
-          x[j][r] = (j0 + j < n && f < D) ? po[(int64_t)(s0 + j0 + j) * D + f] : 0.f;
+        for (int j = 0; j < SB; ++j)
+#pragma unroll
+          for (int r = 0; r < FPL; ++r) {
+            const int f = lane + 64 * r;
+            x[j][r] = (j0 + j < n && f < D) ? po[(int64_t)(s0 + j0 + j) * D + f] : 0.f;
+          }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const float wj =
+              (j0 + j < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j0 + j))
+                           : 0.f;
+#pragma unroll
+          for (int r = 0; r < FPL; ++r) O[r] = __builtin_fmaf(x[j][r], wj, O[r]);
         }
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const float wj =
-            (j0 + j < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j0 + j))
-                         : 0.f;
-#pragma unroll
-        for (int r = 0; r < FPL; ++r) O[r] = __builtin_fmaf(x[j][r], wj, O[r]);
       }
     }
   }
