@@ -270,7 +270,7 @@ def cpu_baseline(w: W.Workload, pairs_row: np.ndarray, target_s: float):
         if w.prenorm:
             oracle.prenorm_rows(args["x"], args["k"], args["v"], args["gamma"], args["beta"],
                                 w.eps, rows, residual=args["residual"], kind=w.kind, lens=w.lens,
-                                add=add64, scale=w.scale, qfmt=w.dtype)
+                                add=add64, scale=w.scale)
         else:
             oracle.mha_rows(args["q"], args["k"], args["v"], rows, w.kind, w.lens, add64,
                             w.scale)

@@ -53,11 +53,10 @@ def _load():
                             ctypes.c_uint32),
         "oracle_probs_row": ([_dp, _dp, _ip, _dp, _u, _i, _i, _i, _i, _i, _d, _i, _i, _i, _dp],
                              ctypes.c_uint32),
-        "oracle_round": ([_d, _i], _d),
-        "oracle_layernorm": ([_dp, _dp, _dp, _d, _l, _i, _i, _dp], None),
-        "oracle_prenorm_rows": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _i, _dp, _i, _i, _i,
+        "oracle_layernorm": ([_dp, _dp, _dp, _d, _l, _i, _dp], None),
+        "oracle_prenorm_rows": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _dp, _i, _i, _i,
                                  _i, _i, _d, _lp, _l, _dp], ctypes.c_uint32),
-        "oracle_prenorm_cross_fwd": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _i, _dp, _i, _i,
+        "oracle_prenorm_cross_fwd": ([_dp, _dp, _dp, _ip, _dp, _u, _dp, _dp, _d, _dp, _i, _i,
                                       _i, _i, _i, _d, _dp], ctypes.c_uint32),
         "oracle_mask_decisions": ([_ip, _dp, _u, _i, _i, _i, _i, _bp], None),
         "oracle_softmax_rows": ([_dp, _l, _i, _d, _dp], ctypes.c_uint32),
@@ -159,25 +158,15 @@ def probs_row(q, k, b, h, i, kind=0, lens=None, add=None, scale=None):
     return p, int(f)
 
 
-QFMT = {None: 0, "f32": 1, "f16": 2, "bf16": 3}
-
-
-def round_to(x, fmt):
-    """Round float64 values to nearest-even in fmt ('f32', 'f16', 'bf16')."""
-    f = _load().oracle_round
-    code = QFMT[fmt]
-    return np.vectorize(lambda t: f(float(t), code), otypes=[np.float64])(np.asarray(x))
-
-
-def layernorm(x, gamma, beta, eps, qfmt=None):
-    """Per-token LayerNorm over the last axis of x (result rounded to qfmt)."""
+def layernorm(x, gamma, beta, eps):
+    """Per-token LayerNorm over the last axis of x, in fp64."""
     x = _f64(x)
     F = x.shape[-1]
     gamma = _f64(gamma, (F,))
     beta = _f64(beta, (F,))
     y = np.empty_like(x)
     _load().oracle_layernorm(_ptr(x, _dp), _ptr(gamma, _dp), _ptr(beta, _dp), float(eps),
-                             x.size // F, F, QFMT[qfmt], _ptr(y, _dp))
+                             x.size // F, F, _ptr(y, _dp))
     return y
 
 
@@ -198,22 +187,21 @@ def _prenorm_common(x, k, v, gamma, beta, residual, kind, lens, add, scale):
 
 
 def prenorm_cross_fwd(x, k, v, gamma, beta, eps, residual=None, kind=0, lens=None, add=None,
-                      scale=None, qfmt=None):
+                      scale=None):
     """Full pre-LN cross-attention. x [B,Lq,H*D] -> (out [B,Lq,H*D], flags).
-    qfmt ('f32'/'f16'/'bf16'/None): the working precision the normalised Q is
-    held in."""
+    The normalised query is used in fp64 as computed (no rounding step)."""
     x, k, v, gamma, beta, residual, lens, add, scale, (B, H, Lq, Lk, D) = _prenorm_common(
         x, k, v, gamma, beta, residual, kind, lens, add, scale)
     out = np.empty((B, Lq, H * D), np.float64)
     f = _load().oracle_prenorm_cross_fwd(
         _ptr(x, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip), _ptr(add, _dp), kind,
-        _ptr(gamma, _dp), _ptr(beta, _dp), float(eps), QFMT[qfmt], _ptr(residual, _dp), B, H, Lq,
+        _ptr(gamma, _dp), _ptr(beta, _dp), float(eps), _ptr(residual, _dp), B, H, Lq,
         Lk, D, scale, _ptr(out, _dp))
     return out, int(f)
 
 
 def prenorm_rows(x, k, v, gamma, beta, eps, rows, residual=None, kind=0, lens=None, add=None,
-                 scale=None, qfmt=None):
+                 scale=None):
     """Selected rows (b, i, h) of the pre-LN cross-attention -> (out [n,D], flags)."""
     x, k, v, gamma, beta, residual, lens, add, scale, (B, H, Lq, Lk, D) = _prenorm_common(
         x, k, v, gamma, beta, residual, kind, lens, add, scale)
@@ -221,7 +209,7 @@ def prenorm_rows(x, k, v, gamma, beta, eps, rows, residual=None, kind=0, lens=No
     out = np.empty((rows.shape[0], D), np.float64)
     f = _load().oracle_prenorm_rows(
         _ptr(x, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(lens, _ip), _ptr(add, _dp), kind,
-        _ptr(gamma, _dp), _ptr(beta, _dp), float(eps), QFMT[qfmt], _ptr(residual, _dp), B, H,
+        _ptr(gamma, _dp), _ptr(beta, _dp), float(eps), _ptr(residual, _dp), B, H,
         Lq, Lk, D, scale, _ptr(rows, _lp), rows.shape[0], _ptr(out, _dp))
     return out, int(f)
 

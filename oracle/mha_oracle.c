@@ -116,31 +116,6 @@ static uint32_t length_flags(unsigned kind, const int32_t* lens, int B, int Lk) 
     return f;
 }
 
-/* Round x to nearest (ties to even) in a binary floating format with p
- * significand bits, smallest normal exponent emin and largest finite value
- * maxv: the plain definition (spacing 2^(e - p + 1) at the leading exponent
- * e, clamped at emin for subnormals; beyond maxv after rounding -> inf).
- * fmt: 0 none, 1 float32, 2 float16, 3 bfloat16. */
-double oracle_round(double x, int fmt) {
-    int p, emin;
-    double maxv;
-    switch (fmt) {
-        case 1: p = 24; emin = -126; maxv = 3.4028234663852886e38; break;
-        case 2: p = 11; emin = -14; maxv = 65504.0; break;
-        case 3: p = 8; emin = -126; maxv = 3.3895313892515355e38; break;
-        default: return x;
-    }
-    if (!isfinite(x) || x == 0.0) return x;
-    int e;
-    frexp(x, &e); /* |x| in [2^(e-1), 2^e) */
-    int lead = e - 1;
-    if (lead < emin) lead = emin;
-    double spacing = ldexp(1.0, lead - (p - 1));
-    double r = nearbyint(x / spacing) * spacing; /* default mode: nearest, ties to even */
-    if (fabs(r) > maxv) r = copysign(INFINITY, x);
-    return r;
-}
-
 /* One attention row: scores, mask, then the naive three-pass softmax of
  * [MAX 2.1] (pass 1 the row max, pass 2 the sum of exp(s - max), pass 3 the
  * normalised weights applied to V). s is caller scratch of length Lk; p, when
@@ -259,7 +234,7 @@ uint32_t oracle_probs_row(const double* q, const double* k, const int32_t* lens,
 /* Pre-LayerNorm of one token of F features [LNXA answer step 2]: mean, biased
  * variance, (x - mean) / sqrt(var + eps), then gamma and beta. */
 static void layernorm_token(const double* x, const double* gamma, const double* beta,
-                            double eps, int F, int qfmt, double* y) {
+                            double eps, int F, double* y) {
     double mean = 0.0;
     for (int f = 0; f < F; ++f) mean += x[f];
     mean /= F;
@@ -267,26 +242,25 @@ static void layernorm_token(const double* x, const double* gamma, const double* 
     for (int f = 0; f < F; ++f) var += (x[f] - mean) * (x[f] - mean);
     var /= F;
     double inv = 1.0 / sqrt(var + eps);
-    for (int f = 0; f < F; ++f) y[f] = oracle_round((x[f] - mean) * inv * gamma[f] + beta[f], qfmt);
+    for (int f = 0; f < F; ++f) y[f] = (x[f] - mean) * inv * gamma[f] + beta[f];
 }
 
 void oracle_layernorm(const double* x, const double* gamma, const double* beta, double eps,
-                      int64_t ntok, int F, int qfmt, double* y) {
+                      int64_t ntok, int F, double* y) {
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < ntok; ++t)
-        layernorm_token(x + t * F, gamma, beta, eps, F, qfmt, y + t * F);
+        layernorm_token(x + t * F, gamma, beta, eps, F, y + t * F);
 }
 
 /* Pre-LN cross-attention for selected rows: rows holds n triples (b, i, h);
  * out receives n*D values out[b, i, h*D + d] = attention + residual.
  * x, residual [B,Lq,H*D]; k, v [B,H,Lk,D]; gamma, beta [H*D]. residual may be NULL.
- * qfmt: the normalised query is held in the working precision of the call
- * (FP16/BF16 mixed precision, gamma and beta applied straight onto the Q
- * matrix with half-precision FMAs [LNXA knowledge points; answer step 2]),
- * so it is rounded to that format (oracle_round) before the attention. */
+ * The normalised query enters the attention exactly as computed, in fp64: the
+ * plain definition has no rounding step between the LayerNorm and the scores
+ * [LNXA answer step 2: Q = LN(x) feeds S = Q K^T]. */
 uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
                              const int32_t* lens, const double* add, unsigned kind,
-                             const double* gamma, const double* beta, double eps, int qfmt,
+                             const double* gamma, const double* beta, double eps,
                              const double* residual, int B, int H, int Lq, int Lk, int D,
                              double scale, const int64_t* rows, int64_t n, double* out) {
     uint32_t flags = length_flags(kind, lens, B, Lk);
@@ -299,7 +273,7 @@ uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
         for (int64_t r = 0; r < n; ++r) {
             int64_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
             int64_t tok = b * Lq + i, bh = b * H + h;
-            layernorm_token(x + tok * F, gamma, beta, eps, F, qfmt, y);
+            layernorm_token(x + tok * F, gamma, beta, eps, F, y);
             const double* addrow = mask_row(add, kind, b, h, H, Lq, Lk, i);
             int64_t len_b = (kind & OR_PADDING) ? lens[b] : Lk;
             double* o = out + r * D;
@@ -319,7 +293,7 @@ uint32_t oracle_prenorm_rows(const double* x, const double* k, const double* v,
 /* Full pre-LN cross-attention: out [B,Lq,H*D]. */
 uint32_t oracle_prenorm_cross_fwd(const double* x, const double* k, const double* v,
                                   const int32_t* lens, const double* add, unsigned kind,
-                                  const double* gamma, const double* beta, double eps, int qfmt,
+                                  const double* gamma, const double* beta, double eps,
                                   const double* residual, int B, int H, int Lq, int Lk, int D,
                                   double scale, double* out) {
     int64_t n = (int64_t)B * Lq * H;
@@ -330,7 +304,7 @@ uint32_t oracle_prenorm_cross_fwd(const double* x, const double* k, const double
         rows[3 * r + 2] = r % H;
     }
     /* row r = ((b*Lq + i)*H + h) lands at out + r*D, i.e. out[b, i, h*D + d] */
-    uint32_t f = oracle_prenorm_rows(x, k, v, lens, add, kind, gamma, beta, eps, qfmt, residual,
+    uint32_t f = oracle_prenorm_rows(x, k, v, lens, add, kind, gamma, beta, eps, residual,
                                      B, H, Lq, Lk, D, scale, rows, n, out);
     free(rows);
     return f;

@@ -100,7 +100,7 @@ def run_oracle(w: W.Workload):
         return oracle.prenorm_cross_fwd(x, w.f64("k"), w.f64("v"), w.f64("gamma"),
                                         w.f64("beta"), w.eps, residual=x if w.residual else None,
                                         kind=w.kind, lens=w.lens, add=w.f64("add"),
-                                        scale=w.scale, qfmt=w.dtype)
+                                        scale=w.scale)
     return oracle.mha_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.kind, w.lens, w.f64("add"),
                           w.scale)
 
@@ -111,7 +111,7 @@ def oracle_rows(w: W.Workload, rows):
         x = w.f64("x")
         return oracle.prenorm_rows(x, w.f64("k"), w.f64("v"), w.f64("gamma"), w.f64("beta"),
                                    w.eps, rows, residual=x if w.residual else None, kind=w.kind,
-                                   lens=w.lens, add=w.f64("add"), scale=w.scale, qfmt=w.dtype)
+                                   lens=w.lens, add=w.f64("add"), scale=w.scale)
     return oracle.mha_rows(w.f64("q"), w.f64("k"), w.f64("v"), rows, w.kind, w.lens,
                            w.f64("add"), w.scale)
 

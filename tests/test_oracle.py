@@ -388,67 +388,3 @@ def test_fp16_min_mask_is_a_finite_bias_not_a_mask():
     add = np.full((1, 1, 1, 3), -65504.0)
     out, f = oracle.mha_fwd(q, k, v, ADDITIVE, None, add)
     assert f == 0 and abs(out[0, 0, 0, 0] - 3.0) < 1e-13
-
-
-# --------------------------------------------------------------------------
-# rounding of the pre-LN query to the working precision
-# --------------------------------------------------------------------------
-def test_round_matches_numpy_and_bit_rounding():
-    rng = np.random.default_rng(21)
-    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 6, 4000),
-                        [0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 1e-8, 6e-8, 2.0 ** -24,
-                         3 * 2.0 ** -25, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, np.inf, -np.inf]])
-    with np.errstate(over="ignore"):
-        np.testing.assert_array_equal(oracle.round_to(x, "f16"), x.astype(np.float16).astype(float))
-        np.testing.assert_array_equal(oracle.round_to(x, "f32"), x.astype(np.float32).astype(float))
-    # bfloat16: for inputs that are already float32 values, rounding the float32
-    # bit pattern to its upper 16 bits (nearest, ties to even) is the definition
-    x32 = x[np.isfinite(x)].astype(np.float32)
-    bits = x32.view(np.uint32).astype(np.uint64)
-    r = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
-    ref = r.astype(np.uint32).view(np.float32).astype(float)
-    np.testing.assert_array_equal(oracle.round_to(x32.astype(float), "bf16"), ref)
-    assert np.isnan(oracle.round_to(np.array([np.nan]), "f16")).all()
-
-
-def _round_independent(y, fmt):
-    """f16: numpy's correctly rounded conversion. bf16: nearest-even on the
-    upper 16 bits of the float32 value. Rounding first to float32 can only
-    change the bf16 result when the float32 value lands exactly on a bf16 tie
-    (low 16 bits 0x8000); those few are settled against the float64 value
-    (the two bf16 neighbours and y are exact in float64, so the distances are
-    exact)."""
-    if fmt == "f16":
-        return y.astype(np.float16).astype(np.float64)
-    y32 = y.astype(np.float32)
-    bits = y32.view(np.uint32).astype(np.uint64)
-    r = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
-    for idx in zip(*np.nonzero((bits & 0xFFFF) == 0x8000)):
-        t = int(bits[idx])
-        lo = np.array([(t >> 16) << 16], np.uint64).astype(np.uint32).view(np.float32)[0]
-        hi = np.array([((t >> 16) + 1) << 16], np.uint64).astype(np.uint32).view(np.float32)[0]
-        dlo, dhi = abs(y[idx] - float(lo)), abs(y[idx] - float(hi))
-        if dlo != dhi:
-            out[idx] = float(lo) if dlo < dhi else float(hi)
-        else:
-            out[idx] = float(lo) if ((t >> 16) & 1) == 0 else float(hi)
-    return out
-
-
-@pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_prenorm_rounded_query_vs_torch(fmt):
-    torch = _torch()
-    w = W.config(4, B=2, H=2, Lq=40, Lk=33, dtype=fmt)
-    x, k, v = w.f64("x"), w.f64("k"), w.f64("v")
-    g, bt = w.f64("gamma"), w.f64("beta")
-    out, _ = oracle.prenorm_cross_fwd(x, k, v, g, bt, w.eps, residual=x, qfmt=fmt)
-    tx = torch.from_numpy(x)
-    y = torch.nn.functional.layer_norm(tx, (w.H * w.D,), torch.from_numpy(g),
-                                       torch.from_numpy(bt), w.eps).numpy()
-    y = torch.from_numpy(_round_independent(y, fmt))  # the working-precision query
-    qh = y.reshape(w.B, w.Lq, w.H, w.D).permute(0, 2, 1, 3)
-    o = torch.nn.functional.scaled_dot_product_attention(qh, torch.from_numpy(k),
-                                                         torch.from_numpy(v), scale=w.scale)
-    ref = (o.permute(0, 2, 1, 3).reshape(w.B, w.Lq, w.H * w.D) + tx).numpy()
-    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-11)
