@@ -12,8 +12,9 @@ Prints one JSON line: metric, value (effective TFLOP/s, masked-out work not
 counted), us_per_call, the roofline of the kernel and the fp64 CPU oracle's
 rate on the host cores (cpu_baseline). For HBM-bound workloads a cold-cache
 figure is added (cold_cache): the median per-call time with the caches flushed
-before each call. ``--config N`` picks workload N (default 2: fp32 B=4 H=8
-L=128 D=64, causal + key padding).
+before each call. ``--config N`` picks workload N. The default is workload 4,
+the largest single-GPU configuration: pre-LayerNorm cross-attention, bfloat16,
+B=32 H=16 Lq=Lk=2048 D=64 (model width 1024), residual added, no mask.
 """
 from __future__ import annotations
 
@@ -312,7 +313,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2,
+    ap.add_argument("--config", type=int, default=4,
                     choices=sorted(W.CONFIGS) + [SOFTMAX_CONFIG_ID, DECODE_CONFIG_ID,
                                                  BWD_CONFIG_ID],
                     help=f"workload; {SOFTMAX_CONFIG_ID} = the row softmax of a materialised "

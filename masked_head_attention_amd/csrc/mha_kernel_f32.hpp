@@ -167,11 +167,23 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
     }
   }
 
+  // ---- key limits (mask decisions that are whole ranges) ----
+  // The padding length is read before any K/V load: the buffers below end at
+  // it, so key rows past a sequence's length are never fetched (they read as
+  // zeros) and whatever that memory holds cannot reach a legal output
+  // [MMHA 3.1: keys past the length do not take part].
+  int kpad = Lk;
+  if (p.kind & K_PADDING) {
+    const int L = p.lens[b];
+    kpad = L < 0 ? 0 : (L > Lk ? Lk : L);
+    if ((L < 0 || L > Lk) && h == 0 && qblk == 0 && tid == 0) atomicOr(p.flags, F_BAD_LENGTH);
+  }
+
   // ---- this wave's K/V rows and additive-mask entries of a step ----
   const __amdgpu_buffer_rsrc_t krs =
-      make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+      make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)kpad * RB));
   const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+      make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)kpad * RB));
   // additive mask: 4 consecutive keys per lane and 16-key tile, one buffer per
   // workgroup (wave-uniform); rows past Lq fall outside it. Loads are
   // 16 bytes at 4-byte alignment; entries at keys >= Lk (the next row's) are
@@ -218,18 +230,10 @@ __global__ __launch_bounds__(64 * F32Cfg<D>::NK) void mha_f32_kernel(const Param
                                                0, 0);
     }
   };
-  // Step 0 before the padding length is known: the causal bound alone.
-  const int kend0 = causal ? min(q0 + BM, Lq) : Lk;
+  const int kend0 = causal ? min(min(q0 + BM, Lq), kpad) : kpad;
   const bool issued0 = ks * BN < kend0;
   if (issued0) issue_step(ks * BN, 0);
 
-  // ---- key limits (mask decisions that are whole ranges) ----
-  int kpad = Lk;
-  if (p.kind & K_PADDING) {
-    const int L = p.lens[b];
-    kpad = L < 0 ? 0 : (L > Lk ? Lk : L);
-    if ((L < 0 || L > Lk) && h == 0 && qblk == 0 && tid == 0) atomicOr(p.flags, F_BAD_LENGTH);
-  }
   int kend = kpad;  // keys >= kend are masked for every row of the block
   if (causal) kend = min(kend, min(q0 + BM - 1, Lq - 1) + 1);
   const int nsteps = (kend + BNT - 1) / BNT;

@@ -249,7 +249,13 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   const int64_t bh = (int64_t)b * H + h;
 
   // ---- Q fragments: Q[qi][16c + 8hh + j] (B operand of S^T = K Q^T) ----
+  // Pre-LN: the normalised query is formed in fp32 and carried as two 16-bit
+  // parts, hi = round(q) and lo = round(q - hi), each multiplied into the same
+  // fp32 accumulator. That keeps about twice the type's significant bits
+  // (relative error ~2^-17 for bfloat16), so the scores see the query the
+  // LayerNorm defines [LNXA answer step 2] rather than its 16-bit rounding.
   Frag8<T> qf[NC];
+  Frag8<T> qlo[PRENORM ? NC : 1];
   if constexpr (!PRENORM) {
     const char* qrow = (const char*)p.q + ((bh * Lq + (row_ok ? qi : 0)) * D) * E;
 #pragma unroll
@@ -263,22 +269,29 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int off = (16 * c + 8 * hh) * E;
-      if (!row_ok) { qf[c] = zero8<T>(); continue; }
-      float xv[8], gv[8], bv[8], qv[8];
+      if (!row_ok) { qf[c] = zero8<T>(); qlo[c] = zero8<T>(); continue; }
+      float xv[8], gv[8], bv[8], qv[8], hv[8];
       unpack8(ld_global8<T>(xrow + off), xv);
       unpack8(ld_global8<T>(grow + off), gv);
       unpack8(ld_global8<T>(brow + off), bv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) qv[j] = (xv[j] - ms.x) * ms.y * gv[j] + bv[j];
       qf[c] = pack8<T>(qv);
+      unpack8(qf[c], hv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] -= hv[j];  // exact in fp32
+      qlo[c] = pack8<T>(qv);
     }
   }
 
-  // ---- K/V tiles: HBM -> LDS directly ----
+  // ---- K/V tiles: HBM -> LDS directly. The buffers end at the padding
+  // length (Lk without PADDING): key rows past a sequence's length are never
+  // fetched and read as zeros, so whatever that memory holds cannot reach a
+  // legal output [MMHA 3.1: keys past the length do not take part] ----
   const __amdgpu_buffer_rsrc_t krs =
-      make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+      make_rsrc((const char*)p.k + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)kpad * RB));
   const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)Lk * RB));
+      make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)kpad * RB));
   const int wid = tid >> 6;  // wave index in the workgroup
   auto issue_tile = [&](int kt0, int buf) {
 #pragma unroll
@@ -479,6 +492,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           Frag8<T> kf;
           kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
           s[blk] = mma8(kf, qf[cc], s[blk]);
+          if constexpr (PRENORM) s[blk] = mma8(kf, qlo[cc], s[blk]);
         }
       __builtin_amdgcn_s_setprio(0);
       // online softmax over the tile [MAX 2.3]. ADD: s becomes the logit

@@ -103,34 +103,3 @@ def run_oracle(w: W.Workload):
                                         scale=w.scale)
     return oracle.mha_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.kind, w.lens, w.f64("add"),
                           w.scale)
-
-
-def oracle_rows(w: W.Workload, rows):
-    """Rows are (b, h, i) for self-attention, (b, i, h) for pre-LN."""
-    if w.prenorm:
-        x = w.f64("x")
-        return oracle.prenorm_rows(x, w.f64("k"), w.f64("v"), w.f64("gamma"), w.f64("beta"),
-                                   w.eps, rows, residual=x if w.residual else None, kind=w.kind,
-                                   lens=w.lens, add=w.f64("add"), scale=w.scale)
-    return oracle.mha_rows(w.f64("q"), w.f64("k"), w.f64("v"), rows, w.kind, w.lens,
-                           w.f64("add"), w.scale)
-
-
-def sample_rows(w: W.Workload, n: int, seed: int = 0):
-    """n sampled rows plus the corners (first/last row of first/last head/batch)."""
-    rng = np.random.default_rng(seed)
-    B, H, L = w.B, w.H, w.Lq
-    corners = [(0, 0, 0), (B - 1, H - 1, L - 1), (0, H - 1, L - 1), (B - 1, 0, 0),
-               (0, 0, min(L - 1, 127)), (B - 1, H - 1, max(0, L - 33))]
-    rnd = [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(L))) for _ in range(n)]
-    rows = sorted(set(corners + rnd))
-    if w.prenorm:
-        return np.array([(b, i, h) for b, h, i in rows], np.int64)
-    return np.array(rows, np.int64)
-
-
-def gather_rows(w: W.Workload, out: np.ndarray, rows: np.ndarray) -> np.ndarray:
-    if w.prenorm:
-        D = w.D
-        return np.stack([out[b, i, h * D:(h + 1) * D] for b, i, h in rows])
-    return np.stack([out[b, h, i] for b, h, i in rows])

@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import (TOL, assert_parity, from_dev, gather_rows, gpu_inputs, half_ulp,
-                     oracle_rows, run_gpu, run_oracle, sample_rows, to_dev)
+from helpers import (TOL, assert_parity, from_dev, gpu_inputs, half_ulp, run_gpu,
+                     run_oracle, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -162,21 +162,56 @@ def test_unaligned_additive_rows():
     _check(w, "additive-odd-Lk")
 
 
-# ---- full sizes, sampled rows, in the benchmark's launch configuration -----
+# ---- full sizes, in the benchmark's launch configuration -------------------
+def _nan_out(w):
+    """An output buffer pre-filled with NaN, so a row the kernel never writes
+    fails the comparison."""
+    import torch
+
+    from helpers import torch_dtype
+
+    shape = (w.B, w.Lq, w.H * w.D) if w.prenorm else (w.B, w.H, w.Lq, w.D)
+    return torch.full(shape, float("nan"), dtype=torch_dtype(w.dtype), device="cuda")
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_workload_full_size_sampled(cfg):
+def test_workload_full_size_elementwise(cfg):
+    """Every output element of the full-size workload against the fp64 oracle
+    (the whole grid, including the XCD workgroup remap and the heaviest-first
+    causal order). The pre-LN cross-attention workload (B=32, H=16,
+    Lq=Lk=2048, D=64, bfloat16) is compared against the unrounded oracle."""
     w = W.config(cfg)
-    print(f"[parity] full-size cfg{cfg} {w.name}", flush=True)
-    out_t, flags = run_gpu(w)
-    rows = sample_rows(w, 300, seed=cfg)
-    ref, rflags = oracle_rows(w, rows)
-    got = gather_rows(w, from_dev(out_t), rows)
-    assert_parity(got, ref, w.dtype, f"cfg{cfg}-full-sampled")
-    # the row sample cannot see every row's flag; fully masked rows and bad
-    # lengths are decided over the whole input
-    full = oracle.fully_masked_rows(w.kind, w.B, w.H, w.Lq, w.Lk, w.lens, w.f64("add"))
-    expect = (oracle.FLAG_FULLY_MASKED_ROW if full else 0) | (rflags & oracle.FLAG_BAD_LENGTH)
-    assert flags == expect
+    print(f"[parity] full-size cfg{cfg} {w.name} elementwise", flush=True)
+    out_t, flags = run_gpu(w, out=_nan_out(w))
+    got = from_dev(out_t)
+    del out_t
+    ref, rflags = run_oracle(w)
+    assert_parity(got, ref, w.dtype, f"cfg{cfg}-full")
+    assert flags == rflags
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind,prenorm", [(PADDING, False), (CAUSAL | PADDING, False),
+                                          (PADDING, True)])
+def test_nonfinite_padding_rows_do_not_leak(dtype, D, kind, prenorm):
+    """Key rows at or past a sequence's length do not take part [MMHA 3.1],
+    whatever the memory there holds: K/V rows >= len_b filled with NaN, +inf
+    and -inf must leave every output equal to the oracle's (which never reads
+    them), with no NONFINITE flag. Lengths fall inside tiles, so edge tiles
+    straddle the garbage."""
+    w = W.make("pad-garbage", dtype, B=3, H=2, Lq=90, Lk=200, D=D, kind=kind, seed=31 + D,
+               lens_range=(1, 200), prenorm=prenorm, x_mean=0.5, x_std=3.0, residual=prenorm)
+    w.lens = np.array([37, 130, 1], np.int32)
+    for name in ("k", "v"):
+        a = w.f64(name).copy()
+        for b, L in enumerate(w.lens):
+            a[b, :, L::3] = np.nan
+            a[b, :, L + 1::3] = np.inf
+            a[b, :, L + 2::3] = -np.inf
+        setattr(w, name, W.round_to(a, dtype))
+    assert not np.isfinite(w.f64("v")).all()
+    _check(w, f"pad-garbage-{dtype}-D{D}-k{kind}-pre{int(prenorm)}")
 
 
 # ---- exact decisions: skip counters and the mask probe ---------------------
