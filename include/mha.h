@@ -86,9 +86,17 @@ typedef enum {
     MHA_E_NO_DEVICE = 8,   /* no usable HIP device / runtime error while preparing */
     MHA_E_LAUNCH = 9,      /* the kernel launch itself failed */
     MHA_E_ARG = 10,        /* scale or eps not finite, scale < 0, eps < 0 */
-    MHA_E_WORKSPACE = 11   /* the decode workspace is NULL, not 16-byte aligned or smaller
+    MHA_E_WORKSPACE = 11,  /* the decode workspace is NULL, not 16-byte aligned or smaller
                               than mha_decode_workspace_size reports */
+    MHA_E_NOT_INITIALIZED = 12, /* an allocation-free entry point was called on a device
+                                   where mha_init has not run */
+    MHA_E_SCRATCH = 13     /* an allocation-free call needs more scratch than
+                              MHA_NOALLOC_SCRATCH_BYTES */
 } mha_status;
+
+/* Size of the static scratch array behind the allocation-free entry points:
+ * one copy per GPU the library runs on, held until the process ends. */
+#define MHA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Device flag word bits (ORed by kernels, cleared by mha_get_flags). */
 enum {
@@ -99,9 +107,13 @@ enum {
     MHA_FLAG_BAD_LENGTH = 4        /* a padding length lies outside [0, Lk] */
 };
 
-/* Allocate (once) and zero the current device's flag word. Optional: the
- * first call on a device does it otherwise; call it before capturing launches
- * into a HIP graph so that no allocation happens during capture. */
+/* Set-up of the current device (no passage: library housekeeping).
+ * Allocates (once) and zeroes the device's flag word, and looks up (once) the
+ * device address of its copy of the allocation-free entry points' static
+ * scratch array. Optional for the allocating entry points, whose first call
+ * on a device does the flag word otherwise; required, once per device, before
+ * mha_decode_fwd_noalloc. Call it before capturing launches into a HIP graph
+ * so that nothing is allocated during capture. */
 mha_status mha_init(void);
 
 /* Masked multi-head self/cross attention forward [MMHA 2, 4.2; MAX 2.4].
@@ -183,6 +195,29 @@ mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int
                           int B, int H, int Lk, int D, float scale, mha_dtype dtype,
                           void* workspace, size_t workspace_bytes, void* stream, void* out,
                           float* lse);
+
+/* mha_decode_fwd without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments (minus the workspace), results, validation, flags and launches as
+ * mha_decode_fwd; the per-split partial results go to a static device array
+ * of MHA_NOALLOC_SCRATCH_BYTES per GPU instead.
+ *   - mha_init must have run on the current device first, otherwise
+ *     MHA_E_NOT_INITIALIZED (nothing is enqueued).
+ *   - A call whose mha_decode_workspace_size exceeds MHA_NOALLOC_SCRATCH_BYTES
+ *     fails with MHA_E_SCRATCH before any HIP call.
+ *   - No hipMalloc, hipFree or other allocating routine is called.
+ *   - Every call on a GPU shares that GPU's one scratch array: calls that
+ *     overlap in time on one GPU (other streams, other threads) race and give
+ *     undefined results. Calls ordered on one stream are safe; the array keeps
+ *     the last call's contents, which no call reads before writing. */
+mha_status mha_decode_fwd_noalloc(const void* q, const void* k, const void* v,
+                                  const int32_t* lens, int B, int H, int Lk, int D, float scale,
+                                  mha_dtype dtype, void* stream, void* out, float* lse);
+
+/* *bytes = MHA_NOALLOC_SCRATCH_BYTES (no passage: the limit of the
+ * allocation-free entry points). */
+mha_status mha_noalloc_scratch_bytes(size_t* bytes);
 
 /* Workspace bytes mha_decode_fwd needs for these sizes (0 when every head is
  * one split). Pure host computation: no device is touched. Fails with the

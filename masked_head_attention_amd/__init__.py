@@ -184,6 +184,36 @@ def decode(q, k, v, lens=None, scale: Optional[float] = None, out=None, lse=None
     return out, lse
 
 
+def noalloc_scratch_bytes() -> int:
+    """Size of the per-GPU static scratch array of the allocation-free entry points."""
+    n = ctypes.c_size_t(0)
+    check(lib().mha_noalloc_scratch_bytes(ctypes.byref(n)), "mha_noalloc_scratch_bytes")
+    return int(n.value)
+
+
+def decode_noalloc(q, k, v, lens=None, scale: Optional[float] = None, out=None, lse=None,
+                   stream=None):
+    """decode() through the allocation-free entry point: the library allocates
+    nothing and takes no workspace (the partial results live in its static
+    per-GPU scratch array). init() must have run on the device. ``out`` and
+    ``lse`` must be given (the caller's buffers); lse may be None."""
+    _dev(q, "q")
+    B, H, D = q.shape
+    Lk = k.shape[2]
+    _dev(k, "k", q.dtype, (B, H, Lk, D))
+    _dev(v, "v", q.dtype, (B, H, Lk, D))
+    _dev(lens, "lens", _torch().int32, (B,))
+    if out is None:
+        raise ValueError("decode_noalloc: out must be given (this entry point allocates nothing)")
+    _dev(out, "out", q.dtype, (B, H, D))
+    _dev(lse, "lse", _torch().float32, (B, H))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib().mha_decode_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(lens), B, H, Lk, D, scale,
+                                      _dtype_code(q), _stream(stream), _ptr(out), _ptr(lse))
+    check(st, "mha_decode_fwd_noalloc")
+    return out, lse
+
+
 def bwd_workspace_size(B: int, H: int, Lq: int, dtype_code: int) -> int:
     """Bytes of device workspace that bwd needs (the rows' statistics)."""
     n = ctypes.c_size_t(0)

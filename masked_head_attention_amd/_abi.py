@@ -16,7 +16,8 @@ MASK_NONE, CAUSAL, PADDING, ADDITIVE, KEEP, PER_HEAD = 0, 1, 2, 4, 8, 16
 FLAG_FULLY_MASKED_ROW, FLAG_NONFINITE, FLAG_BAD_LENGTH = 1, 2, 4
 STATUS = {0: "MHA_OK", 1: "MHA_E_NULL", 2: "MHA_E_SHAPE", 3: "MHA_E_DTYPE", 4: "MHA_E_MASK",
           5: "MHA_E_UNSUPPORTED", 6: "MHA_E_ALIGN", 7: "MHA_E_OVERFLOW", 8: "MHA_E_NO_DEVICE",
-          9: "MHA_E_LAUNCH", 10: "MHA_E_ARG", 11: "MHA_E_WORKSPACE"}
+          9: "MHA_E_LAUNCH", 10: "MHA_E_ARG", 11: "MHA_E_WORKSPACE", 12: "MHA_E_NOT_INITIALIZED",
+          13: "MHA_E_SCRATCH"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 _vp, _i, _u, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float
@@ -33,6 +34,8 @@ SIGNATURES = {
     "mha_decode_fwd": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, ctypes.c_size_t, _vp,
                         _vp, _vp], _i),
     "mha_decode_workspace_size": ([_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)], _i),
+    "mha_decode_fwd_noalloc": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp], _i),
+    "mha_noalloc_scratch_bytes": ([ctypes.POINTER(ctypes.c_size_t)], _i),
     "mha_bwd": ([_vp, _vp, _vp, _vp, _vp, _u, _i, _i, _i, _i, _i, _f, _i, _vp, ctypes.c_size_t,
                  _vp, _vp, _vp, _vp], _i),
     "mha_bwd_workspace_size": ([_i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)], _i),

@@ -32,6 +32,14 @@ std::mutex g_mu;
 uint32_t* g_flags[kMaxDevices] = {};
 std::atomic<unsigned long long*> g_counters{nullptr};
 
+// Scratch of the allocation-free entry points: a file-scope device array, one
+// copy per GPU, held for the life of the process. In host code its name is a
+// host-side stand-in, never a device address: the device address of each
+// GPU's copy is looked up once (mha_init, with that device current) and kept
+// in g_scratch; kernels and copies only ever see that pointer.
+static __device__ __align__(256) char scratch[MHA_NOALLOC_SCRATCH_BYTES];
+void* g_scratch[kMaxDevices] = {};
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool mul_ok(int64_t a, int64_t b, int64_t* r) {
@@ -65,6 +73,33 @@ mha_status device_flags(uint32_t** out) {
     g_flags[dev] = static_cast<uint32_t*>(p);
   }
   *out = g_flags[dev];
+  return MHA_OK;
+}
+
+// Look up (once per device, with that device current) the device address of
+// this device's copy of `scratch`. No allocation.
+mha_status device_scratch_setup() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MHA_E_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return MHA_E_NO_DEVICE;
+    g_scratch[dev] = ptr;
+  }
+  return MHA_OK;
+}
+
+// The current device's flag word and scratch address, both set up earlier by
+// mha_init; nothing is allocated or looked up here.
+mha_status device_noalloc_state(uint32_t** flags, void** scr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MHA_E_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_flags[dev] || !g_scratch[dev]) return MHA_E_NOT_INITIALIZED;
+  *flags = g_flags[dev];
+  *scr = g_scratch[dev];
   return MHA_OK;
 }
 
@@ -275,27 +310,35 @@ mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtyp
   return MHA_OK;
 }
 
-mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int32_t* lens,
-                          int B, int H, int Lk, int D, float scale, mha_dtype dtype,
-                          void* workspace, size_t workspace_bytes, void* stream, void* out,
-                          float* lse) {
-  int chunk = 0, nsplit = 0;
-  size_t ws = 0;
-  mha_status st = decode_check(B, H, Lk, D, dtype, &chunk, &nsplit, &ws);
+}  // extern "C"
+
+namespace {
+
+// Decode argument checks shared by both decode entry points (everything but
+// the workspace). *empty is set for a call that has nothing to do.
+mha_status decode_args(const void* q, const void* k, const void* v, const int32_t* lens,
+                       int B, int H, int Lk, int D, float scale, mha_dtype dtype, void* out,
+                       float* lse, int* chunk, int* nsplit, size_t* ws, bool* empty) {
+  mha_status st = decode_check(B, H, Lk, D, dtype, chunk, nsplit, ws);
   if (st != MHA_OK) return st;
   if (!std::isfinite(scale) || scale < 0.f) return MHA_E_ARG;
-  if (B == 0 || H == 0) return MHA_OK;  // empty call
+  *empty = B == 0 || H == 0;
+  if (*empty) return MHA_OK;
   if (!q || !out) return MHA_E_NULL;
   if (Lk > 0 && (!k || !v)) return MHA_E_NULL;
   const void* ptrs16[] = {q, k, v, out};
   for (const void* p : ptrs16)
     if (p && !aligned(p, 16)) return MHA_E_ALIGN;
   if ((lens && !aligned(lens, 4)) || (lse && !aligned(lse, 4))) return MHA_E_ALIGN;
-  if (ws > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < ws))
-    return MHA_E_WORKSPACE;
-  uint32_t* flags = nullptr;
-  st = device_flags(&flags);
-  if (st != MHA_OK) return st;
+  return MHA_OK;
+}
+
+// Enqueue the decode kernels with a validated workspace (ws bytes at `work`).
+mha_status decode_launch(const void* q, const void* k, const void* v, const int32_t* lens,
+                         int B, int H, int Lk, int D, float scale, mha_dtype dtype,
+                         int chunk, int nsplit, size_t ws, void* work, uint32_t* flags,
+                         void* stream, void* out, float* lse) {
+  float* workspace = static_cast<float*>(work);
   mha::DecodeParams p{};
   p.q = q;
   p.k = k;
@@ -304,8 +347,8 @@ mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int
   p.out = out;
   p.lse = lse;
   const int64_t slots = (int64_t)B * H * nsplit;
-  p.part_o = ws > 0 ? static_cast<float*>(workspace) : nullptr;
-  p.part_ml = ws > 0 ? static_cast<float*>(workspace) + slots * D : nullptr;
+  p.part_o = ws > 0 ? workspace : nullptr;
+  p.part_ml = ws > 0 ? workspace + slots * D : nullptr;
   p.B = B;
   p.H = H;
   p.Lk = Lk;
@@ -317,9 +360,60 @@ mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int
   return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
 }
 
+}  // namespace
+
+extern "C" {
+
+mha_status mha_decode_fwd(const void* q, const void* k, const void* v, const int32_t* lens,
+                          int B, int H, int Lk, int D, float scale, mha_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream, void* out,
+                          float* lse) {
+  int chunk = 0, nsplit = 0;
+  size_t ws = 0;
+  bool empty = false;
+  mha_status st = decode_args(q, k, v, lens, B, H, Lk, D, scale, dtype, out, lse, &chunk,
+                              &nsplit, &ws, &empty);
+  if (st != MHA_OK || empty) return st;
+  if (ws > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < ws))
+    return MHA_E_WORKSPACE;
+  uint32_t* flags = nullptr;
+  st = device_flags(&flags);
+  if (st != MHA_OK) return st;
+  return decode_launch(q, k, v, lens, B, H, Lk, D, scale, dtype, chunk, nsplit, ws, workspace,
+                       flags, stream, out, lse);
+}
+
+mha_status mha_decode_fwd_noalloc(const void* q, const void* k, const void* v,
+                                  const int32_t* lens, int B, int H, int Lk, int D, float scale,
+                                  mha_dtype dtype, void* stream, void* out, float* lse) {
+  int chunk = 0, nsplit = 0;
+  size_t ws = 0;
+  bool empty = false;
+  mha_status st = decode_args(q, k, v, lens, B, H, Lk, D, scale, dtype, out, lse, &chunk,
+                              &nsplit, &ws, &empty);
+  if (st != MHA_OK || empty) return st;
+  if (ws > (size_t)MHA_NOALLOC_SCRATCH_BYTES) return MHA_E_SCRATCH;
+  uint32_t* flags = nullptr;
+  void* scr = nullptr;
+  st = device_noalloc_state(&flags, &scr);
+  if (st != MHA_OK) return st;
+  // the split kernel writes every partial result the merge kernel reads, so
+  // the scratch needs no clearing between calls
+  return decode_launch(q, k, v, lens, B, H, Lk, D, scale, dtype, chunk, nsplit, ws, scr, flags,
+                       stream, out, lse);
+}
+
+mha_status mha_noalloc_scratch_bytes(size_t* bytes) {
+  if (!bytes) return MHA_E_NULL;
+  *bytes = MHA_NOALLOC_SCRATCH_BYTES;
+  return MHA_OK;
+}
+
 mha_status mha_init(void) {
   uint32_t* f = nullptr;
-  return device_flags(&f);
+  const mha_status st = device_flags(&f);
+  if (st != MHA_OK) return st;
+  return device_scratch_setup();
 }
 
 mha_status mha_fwd(const void* q, const void* k, const void* v, const void* mask,
@@ -414,6 +508,10 @@ const char* mha_status_str(mha_status s) {
     case MHA_E_LAUNCH: return "MHA_E_LAUNCH: kernel launch failed";
     case MHA_E_ARG: return "MHA_E_ARG: scale or eps out of range";
     case MHA_E_WORKSPACE: return "MHA_E_WORKSPACE: workspace missing, misaligned or too small";
+    case MHA_E_NOT_INITIALIZED:
+      return "MHA_E_NOT_INITIALIZED: call mha_init on this device before an allocation-free entry point";
+    case MHA_E_SCRATCH:
+      return "MHA_E_SCRATCH: the call needs more scratch than MHA_NOALLOC_SCRATCH_BYTES";
   }
   return "unknown mha_status";
 }

@@ -197,6 +197,42 @@ def test_decode_validation(kw, status):
     assert _dec(**kw) == status
 
 
+def _dec_noalloc(q=A, k=A, v=A, lens=None, B=2, H=4, Lk=4096, D=128, scale=0.125, dtype=1,
+                 out=A, lse=None):
+    return _abi.STATUS[_abi.lib().mha_decode_fwd_noalloc(q, k, v, lens, B, H, Lk, D, scale,
+                                                         dtype, None, out, lse)]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), "MHA_E_DTYPE"),
+    (dict(B=-1), "MHA_E_SHAPE"),
+    (dict(D=96), "MHA_E_UNSUPPORTED"),
+    (dict(scale=float("nan")), "MHA_E_ARG"),
+    (dict(q=None), "MHA_E_NULL"),
+    (dict(out=None), "MHA_E_NULL"),
+    (dict(k=A + 8), "MHA_E_ALIGN"),
+    (dict(lens=A + 2), "MHA_E_ALIGN"),
+    (dict(B=1, H=1, Lk=1 << 24, D=128), "MHA_E_OVERFLOW"),
+    # more partial results than the static scratch holds: refused before any HIP call
+    (dict(B=64, H=64, Lk=8192, D=128), "MHA_E_SCRATCH"),
+    (dict(B=0), "MHA_OK"),
+])
+def test_decode_noalloc_validation(kw, status):
+    assert _dec_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit():
+    n = ctypes.c_size_t(0)
+    assert _abi.lib().mha_noalloc_scratch_bytes(ctypes.byref(n)) == 0
+    assert n.value == 16 << 20
+    assert _abi.lib().mha_noalloc_scratch_bytes(None) == _abi.STATUS_CODE["MHA_E_NULL"]
+    # the largest call that fits uses at most that many bytes of partial results
+    st, need = _ws(64, 64, 8192, 128)
+    assert st == "MHA_OK" and need > n.value
+    st, need = _ws(16, 32, 4096, 128)
+    assert st == "MHA_OK" and 0 < need <= n.value
+
+
 def test_decode_workspace_size():
     # one split per head when the cache is short: no workspace
     assert _ws(2, 4, 37, 128) == ("MHA_OK", 0)
