@@ -144,9 +144,11 @@ mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, co
                                  float eps, const void* residual, int B, int H, int Lq, int Lk,
                                  int D, float scale, mha_dtype dtype, void* stream, void* out);
 
-/* Synchronise stream, then copy the current device's flag word to *flags;
- * clear != 0 resets it to 0 afterwards. The word is per device, not per
- * stream: launches on other streams that have not finished are not seen. */
+/* The device error flag [LNXA knowledge points: a global flag the kernel
+ * raises when the softmax goes bad, read back by the host]. Synchronise
+ * stream, then copy the current device's flag word to *flags; clear != 0
+ * resets it to 0 afterwards. The word is per device, not per stream: launches
+ * on other streams that have not finished are not seen. */
 mha_status mha_get_flags(void* stream, uint32_t* flags, int clear);
 
 /* Row softmax of a materialised score tensor [MAX 2.1: the row-softmax
@@ -220,8 +222,9 @@ mha_status mha_decode_fwd_noalloc(const void* q, const void* k, const void* v,
 mha_status mha_noalloc_scratch_bytes(size_t* bytes);
 
 /* Workspace bytes mha_decode_fwd needs for these sizes (0 when every head is
- * one split). Pure host computation: no device is touched. Fails with the
- * same shape/dtype status codes as mha_decode_fwd. */
+ * one split); no passage: the size of the split plan's partial results. Pure
+ * host computation: no device is touched. Fails with the same shape/dtype
+ * status codes as mha_decode_fwd. */
 mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
                                      size_t* bytes);
 
@@ -250,7 +253,8 @@ mha_status mha_bwd(const void* q, const void* k, const void* v, const void* dout
                    float scale, mha_dtype dtype, void* workspace, size_t workspace_bytes,
                    void* stream, void* dq, void* dk, void* dv);
 
-/* Workspace bytes mha_bwd needs: 8 * B * H * Lq. Pure host computation. */
+/* Workspace bytes mha_bwd needs: 8 * B * H * Lq (no passage: the size of the
+ * row statistics the two backward kernels exchange). Pure host computation. */
 mha_status mha_bwd_workspace_size(int B, int H, int Lq, mha_dtype dtype, size_t* bytes);
 
 /* Debug counters [MAX 6: count executions with device atomics]: a device
@@ -261,10 +265,13 @@ mha_status mha_bwd_workspace_size(int B, int H, int Lq, mha_dtype dtype, size_t*
  * is process-wide; the caller owns and zeroes the memory. */
 mha_status mha_set_debug_counters(uint64_t* dev_counters);
 
-/* Tile of the skip decision for a dtype and D: *rows query rows by *keys keys. */
+/* Tile of the skip decision for a dtype and D: *rows query rows by *keys keys
+ * [MMHA 2: whole tiles of masked positions are skipped; the tile size is this
+ * library's, the pages' kernels use 16 x 32]. Pure host computation. */
 mha_status mha_tile_config(mha_dtype dtype, int D, unsigned mask_kind, int* rows, int* keys);
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string). No passage: the
+ * pages report launch errors with printf [MMHA 4.3]; here they are codes. */
 const char* mha_status_str(mha_status s);
 
 #ifdef __cplusplus
