@@ -141,37 +141,24 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   //    lightest last, in dispatch order (work per block grows with its index);
   //  * otherwise: consecutive workgroup ids go to different XCDs (8 of them,
   //    each with its own L2), so ids are remapped to put the query blocks of
-  //    one (b, head) -- which read the same K/V -- on one XCD, in
-  //    consecutive dispatch slots;
-  //  * pre-LN: the head groups of one (b, query block) -- which read the same
-  //    x rows for the token statistics -- are consecutive, then the query
-  //    blocks of b: every workgroup of a batch entry runs on one XCD, the
-  //    statistics rows are fetched from HBM once, and the query blocks of a
-  //    head group still share its K/V in that XCD's L2.
+  //    one (b, head group) -- which read the same K/V (and, for pre-LN, the
+  //    same x rows across head groups) -- on one XCD.
   int b, hg, qblk;
   {
     const int G = (int)gridDim.x;
     const int bid = (int)blockIdx.x;
     const int ngrp = PRENORM ? p.H / p.hg : p.H;
+    int grp;
     if (p.kind & K_CAUSAL) {
-      const int grp = bid % (p.B * ngrp);
+      grp = bid % (p.B * ngrp);
       qblk = p.nqblk - 1 - bid / (p.B * ngrp);
-      b = grp / ngrp;
-      hg = grp % ngrp;
     } else {
       const int L = (G % 8 == 0) ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-      if constexpr (PRENORM) {
-        hg = L % ngrp;
-        const int r = L / ngrp;
-        qblk = r % p.nqblk;
-        b = r / p.nqblk;
-      } else {
-        qblk = L % p.nqblk;
-        const int grp = L / p.nqblk;
-        b = grp / ngrp;
-        hg = grp % ngrp;
-      }
+      qblk = L % p.nqblk;
+      grp = L / p.nqblk;
     }
+    b = grp / ngrp;
+    hg = grp % ngrp;
   }
   const int Lq = p.Lq, Lk = p.Lk, H = p.H;
   const int q0 = qblk * BM;
