@@ -125,6 +125,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   constexpr bool CONV_V = SPLIT_P && (TILE_REGION + VC_BYTES + STAT_BYTES + 16) <= (NK == 1 ? 80 : 160) * 1024;
   constexpr float LOG2E = 1.4426950408889634f;
   constexpr float RESCALE_GAP = 8.0f;         // log2 units
+  constexpr bool LS = PRENORM;                // scores leave the MFMAs in log2 units, less m
   static_assert(NCHUNK % 64 == 0, "tile chunks must fill whole waves");
 
   __shared__ __attribute__((aligned(16))) char smem[TILE_REGION + (CONV_V ? VC_BYTES : 0) + STAT_BYTES + 16];
@@ -254,6 +255,9 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   // fp32 accumulator. That keeps about twice the type's significant bits
   // (relative error ~2^-17 for bfloat16), so the scores see the query the
   // LayerNorm defines [LNXA answer step 2] rather than its 16-bit rounding.
+  // The query is multiplied by scale * log2(e) before the split (no extra
+  // rounding: the pair carries the fp32 product), so the scores come out of
+  // the MFMAs in log2 units.
   Frag8<T> qf[NC];
   Frag8<T> qlo[PRENORM ? NC : 1];
   if constexpr (!PRENORM) {
@@ -267,20 +271,20 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     const char* grow = (const char*)p.gamma + (int64_t)h * D * E;
     const char* brow = (const char*)p.beta + (int64_t)h * D * E;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int off = (16 * c + 8 * hh) * E;
-      if (!row_ok) { qf[c] = zero8<T>(); qlo[c] = zero8<T>(); continue; }
+    for (int cc = 0; cc < NC; ++cc) {
+      const int off = (16 * cc + 8 * hh) * E;
+      if (!row_ok) { qf[cc] = zero8<T>(); qlo[cc] = zero8<T>(); continue; }
       float xv[8], gv[8], bv[8], qv[8], hv[8];
       unpack8(ld_global8<T>(xrow + off), xv);
       unpack8(ld_global8<T>(grow + off), gv);
       unpack8(ld_global8<T>(brow + off), bv);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qv[j] = (xv[j] - ms.x) * ms.y * gv[j] + bv[j];
-      qf[c] = pack8<T>(qv);
-      unpack8(qf[c], hv);
+      for (int j = 0; j < 8; ++j) qv[j] = ((xv[j] - ms.x) * ms.y * gv[j] + bv[j]) * c;
+      qf[cc] = pack8<T>(qv);
+      unpack8(qf[cc], hv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) qv[j] -= hv[j];  // exact in fp32
-      qlo[c] = pack8<T>(qv);
+      qlo[cc] = pack8<T>(qv);
     }
   }
 
@@ -476,12 +480,16 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     auto tile = [&](auto edge_tag, auto vconv_tag) {
       constexpr bool EDGE = decltype(edge_tag)::value;
       constexpr bool VCONV = decltype(vconv_tag)::value;
-      // S^T = K Q^T; the two 32-key accumulator chains are interleaved
+      // S^T = K Q^T; the two 32-key accumulator chains are interleaved.
+      // Pre-LN (LS): Q carries scale * log2(e), and the accumulators start at
+      // -m_ref, the running reference, so each score leaves the MFMAs as the
+      // exponent of its weight, c*s - m, with no FMA per element.
+      const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
       f32x16 s[NB32];
 #pragma unroll
       for (int blk = 0; blk < NB32; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[blk][i] = LS ? -m_ref : 0.f;
       // both MFMA blocks run at raised wave priority: the SIMD's other wave
       // then fills the matrix core's gaps with its softmax arithmetic
       __builtin_amdgcn_s_setprio(1);
@@ -513,7 +521,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
               T* tag = nullptr;
               mv = (i & 1) ? hi_f(w, tag) : lo_f(w, tag);
             }
-            u = __builtin_fmaf(u, p.scale, mv);
+            u = LS ? __builtin_fmaf(mv, LOG2E, u) : __builtin_fmaf(u, p.scale, mv);
           } else if constexpr (EDGE) {
             const int key = kb0 + blk * 32 + (i < 8 ? 8 * hh + i : 8 + 8 * hh + i);
             if (key >= kpad || (causal && key > qi)) u = -INFINITY;
@@ -522,7 +530,8 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
           mt = fmaxf(mt, u);
         }
       mt = pair_max(mt);
-      if constexpr (ADD) mt *= LOG2E;  // to log2 units
+      if constexpr (LS) mt = (mt == -INFINITY) ? -INFINITY : m_ref + mt;  // to absolute log2 units
+      else if constexpr (ADD) mt *= LOG2E;  // to log2 units
       else mt = (mt == -INFINITY) ? -INFINITY : mt * c;
       // raise the reference maximum only when exceeded by more than the gap
       if (__ballot(mt > m_run + RESCALE_GAP) != 0) {
@@ -533,6 +542,14 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
         for (int db = 0; db < ND; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        if constexpr (LS) {
+          // the exponents were taken against m_ref: move them to m_new
+          const float shift = (m_new == -INFINITY) ? 0.f : m_new - m_ref;
+#pragma unroll
+          for (int blk = 0; blk < NB32; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[blk][i] -= shift;
+        }
         m_run = m_new;
       }
       const float m_use = (ADD || EDGE) ? (m_run == -INFINITY ? 0.f : m_run) : m_run;
@@ -546,7 +563,9 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float e;
-          if constexpr (ADD) {
+          if constexpr (LS) {
+            e = exp2_fast(s[blk][i]);  // -inf -> 0
+          } else if constexpr (ADD) {
             e = exp2_fast(__builtin_fmaf(s[blk][i], LOG2E, -m_use));  // -inf -> 0
           } else {
             e = exp2_fast(__builtin_fmaf(s[blk][i], c, -m_use));
