@@ -91,9 +91,15 @@ __device__ inline int swz_v16(int row) {
 // tiles; the heaviest query block's serial chain halves and one workgroup
 // fills a CU, so the heaviest-first launch order balances the causal
 // triangle. The two partial (m, l, O) states merge through LDS.
-template <typename T, int D, bool ADD, bool PRENORM, int NK>
+// AM: the mask tensor's form -- 0 none, 1 rows of 16-byte multiples (read as
+// 16-byte vectors), 2 any other row length (read element by element). The
+// two read paths are separate instantiations so that the element-wise one's
+// scalar loads and waits never enter the vector kernel's schedule.
+template <typename T, int D, int AM, bool PRENORM, int NK>
 __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p) {
   static_assert(sizeof(T) == 2, "16-bit element types only");
+  static_assert(AM >= 0 && AM <= 2, "mask form");
+  constexpr bool ADD = AM != 0;
   constexpr int E = 2;
   constexpr int NQ = 4, NW = NQ * NK, NT = 64 * NW, BM = 128, BN = 64, NB32 = 2;
   constexpr int NC = D / 16;                  // 16-feature slices of QK^T
@@ -329,8 +335,13 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     const int64_t slab = (p.kind & K_PER_HEAD) ? (int64_t)b * H + h : (int64_t)b;
     const char* abase = (const char*)p.add + slab * Lq * (int64_t)Lk * E;
     addrow = abase + (int64_t)(row_ok ? qi : 0) * Lk * E;
-    const int wrows = Lq - qw0 < 0 ? 0 : (Lq - qw0 > 32 ? 32 : Lq - qw0);
-    ars = make_rsrc(abase + (int64_t)qw0 * Lk * E, (uint32_t)((int64_t)wrows * Lk * E));
+    // the wave index comes from the thread id, so the compiler cannot see that
+    // qw0 is the same in every lane; a descriptor built from it would sit in
+    // vector registers and every load through it would loop over lanes
+    const int qwu = __builtin_amdgcn_readfirstlane(qw0);
+    const int wrows = Lq - qwu < 0 ? 0 : (Lq - qwu > 32 ? 32 : Lq - qwu);
+    const int wbytes = __builtin_amdgcn_readfirstlane(wrows * Lk * E);
+    ars = make_rsrc(abase + (int64_t)qwu * Lk * E, (uint32_t)wbytes);
     arow_off = (uint32_t)n * (uint32_t)Lk * E;
   }
   uint4 am_raw[NB32][2], am_nxt[NB32][2];
@@ -340,7 +351,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int key0 = kt0 + blk * 32 + 16 * g + 8 * hh;
-        if (p.add_vec) {
+        if constexpr (AM == 1) {
           dst[blk][g] = __builtin_bit_cast(
               uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, arow_off + (uint32_t)key0 * E, 0, 0));
         } else {

@@ -17,6 +17,18 @@ constexpr int skip_rows() { return sizeof(T) == 2 ? 32 : F32Cfg<D>::BM; }
 template <typename T, int D>
 constexpr int skip_keys() { return sizeof(T) == 2 ? 64 : F32Cfg<D>::SUB; }
 
+// 16-bit types: 8 waves with two key splits under a causal mask, else 4
+template <typename T, int D, int AM, bool PRE>
+hipError_t launch_half(const Params& p, long long grid, hipStream_t stream) {
+  if (p.kind & K_CAUSAL)
+    hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 2>), dim3((unsigned)grid), dim3(512), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 1>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool ADD, bool PRE>
 hipError_t launch_one(Params p, hipStream_t stream) {
   p.nqblk = (p.Lq + block_rows<T, D>() - 1) / block_rows<T, D>();
@@ -27,12 +39,12 @@ hipError_t launch_one(Params p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (sizeof(T) == 2) {
-    if (p.kind & K_CAUSAL)
-      hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE, 2>), dim3((unsigned)grid), dim3(512),
-                         0, stream, p);
-    else
-      hipLaunchKernelGGL((mha_half_kernel<T, D, ADD, PRE, 1>), dim3((unsigned)grid), dim3(256),
-                         0, stream, p);
+    if constexpr (ADD) {
+      if (p.add_vec) return launch_half<T, D, 1, PRE>(p, grid, stream);
+      return launch_half<T, D, 2, PRE>(p, grid, stream);
+    } else {
+      return launch_half<T, D, 0, PRE>(p, grid, stream);
+    }
   } else {
     hipLaunchKernelGGL((mha_f32_kernel<D, ADD, PRE>), dim3((unsigned)grid),
                        dim3(64 * F32Cfg<D>::NK), 0, stream, p);
