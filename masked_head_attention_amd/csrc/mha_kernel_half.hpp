@@ -132,12 +132,21 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   constexpr float LOG2E = 1.4426950408889634f;
   constexpr float RESCALE_GAP = 8.0f;         // log2 units
   constexpr bool LS = PRENORM;                // scores leave the MFMAs in log2 units, less m
+  // Pre-LN: the normalised query is rounded once, to float16 (11 significant
+  // bits), whatever the call dtype; bfloat16 K tiles are rewritten into
+  // float16 in place once landed, so Q K^T is one float16 MFMA per 16
+  // features. A tile holding a finite |k| > 65504 is re-loaded as bfloat16
+  // and multiplied by the same float16 query split exactly into two
+  // bfloat16 parts.
+  constexpr bool CONV_K = PRENORM && SPLIT_P;
+  using QT = std::conditional_t<PRENORM, _Float16, T>;  // type of the Q fragments
   static_assert(NCHUNK % 64 == 0, "tile chunks must fill whole waves");
 
   __shared__ __attribute__((aligned(16))) char smem[TILE_REGION + (CONV_V ? VC_BYTES : 0) + STAT_BYTES + 16];
   char* const vc_lds = smem + TILE_REGION;                              // converted V, [buf][split]
   char* const stat_lds = smem + TILE_REGION + (CONV_V ? VC_BYTES : 0);
   int* const vflag = reinterpret_cast<int*>(stat_lds + STAT_BYTES);    // [buf]: tag of a tile that fell back
+  int* const kflag = vflag + 2;                                          // [buf]: same for K
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (tid >> 6) % NQ, ks = (tid >> 6) / NQ;  // query group, key split
@@ -256,16 +265,12 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   const int64_t bh = (int64_t)b * H + h;
 
   // ---- Q fragments: Q[qi][16c + 8hh + j] (B operand of S^T = K Q^T) ----
-  // Pre-LN: the normalised query is formed in fp32 and carried as two 16-bit
-  // parts, hi = round(q) and lo = round(q - hi), each multiplied into the same
-  // fp32 accumulator. That keeps about twice the type's significant bits
-  // (relative error ~2^-17 for bfloat16), so the scores see the query the
-  // LayerNorm defines [LNXA answer step 2] rather than its 16-bit rounding.
-  // The query is multiplied by scale * log2(e) before the split (no extra
-  // rounding: the pair carries the fp32 product), so the scores come out of
-  // the MFMAs in log2 units.
-  Frag8<T> qf[NC];
-  Frag8<T> qlo[PRENORM ? NC : 1];
+  // Pre-LN: the normalised query [LNXA answer step 2] is formed in fp32,
+  // multiplied by scale * log2(e) (so the scores come out of the MFMAs in
+  // log2 units) and rounded once to float16, whose 11 significant bits keep
+  // it within a small part of the tolerance for either call dtype; bfloat16
+  // (8 bits) would not.
+  Frag8<QT> qf[NC];
   if constexpr (!PRENORM) {
     const char* qrow = (const char*)p.q + ((bh * Lq + (row_ok ? qi : 0)) * D) * E;
 #pragma unroll
@@ -279,18 +284,14 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       const int off = (16 * cc + 8 * hh) * E;
-      if (!row_ok) { qf[cc] = zero8<T>(); qlo[cc] = zero8<T>(); continue; }
-      float xv[8], gv[8], bv[8], qv[8], hv[8];
+      if (!row_ok) { qf[cc] = zero8<QT>(); continue; }
+      float xv[8], gv[8], bv[8], qv[8];
       unpack8(ld_global8<T>(xrow + off), xv);
       unpack8(ld_global8<T>(grow + off), gv);
       unpack8(ld_global8<T>(brow + off), bv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) qv[j] = ((xv[j] - ms.x) * ms.y * gv[j] + bv[j]) * c;
-      qf[cc] = pack8<T>(qv);
-      unpack8(qf[cc], hv);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[j] -= hv[j];  // exact in fp32
-      qlo[cc] = pack8<T>(qv);
+      qf[cc] = pack8<QT>(qv);
     }
   }
 
@@ -303,7 +304,8 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc((const char*)p.v + bh * (int64_t)Lk * RB, (uint32_t)((int64_t)kpad * RB));
   const int wid = tid >> 6;  // wave index in the workgroup
-  auto issue_tile = [&](int kt0, int buf) {
+  // only_k: the K chunks alone (a K tile fetched again)
+  auto issue_tile = [&](int kt0, int buf, bool only_k) {
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int u0 = it * NT + wid * 64;
@@ -319,8 +321,9 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       const int lcv = phys ^ swz_v16<CPR>(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, MHA_LDS_PTR(void, kl + 16 * u1), 16,
                                                goff + 16 * lck, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 16 * u1), 16,
-                                               goff + 16 * lcv, 0, 0, 0);
+      if (!only_k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, MHA_LDS_PTR(void, vl + 16 * u1), 16,
+                                                 goff + 16 * lcv, 0, 0, 0);
     }
   };
 
@@ -405,6 +408,33 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     if (__ballot(big) != 0 && lane == 0) vflag[b] = tag;
   };
 
+  // bf16 -> f16 rewrite in place of the K tile in buffer b (pre-LN): each
+  // thread rewrites the chunks it loaded itself; a finite |k| > 65504 marks
+  // the tile with `tag`
+  auto convert_k = [&](int b, int tag) {
+    bool big = false;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int u = it * NT + tid;
+      if (NCHUNK % NT != 0 && u >= NCHUNK) break;
+      const int sp = u / (BN * CPR), u1 = u - sp * (BN * CPR);
+      char* const a = smem + b * BUF_BYTES + sp * SPLIT_BYTES + 16 * u1;
+      const uint4 x = lds_load16(a);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      uint32_t r[4];
+      __bf16* tb = nullptr;
+      _Float16* th = nullptr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a0 = lo_f(w[i], tb), a1 = hi_f(w[i], tb);
+        big |= fmaxf(fabsf(a0), fabsf(a1)) > 65504.f;
+        r[i] = pack2(a0, a1, th);
+      }
+      *reinterpret_cast<uint4*>(a) = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+    if (__ballot(big) != 0 && lane == 0) kflag[b] = tag;
+  };
+
   f32x16 o[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db)
@@ -414,13 +444,13 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   int ncomp = 0;
 
   if (ntiles > 0) {
-    issue_tile(0, 0);
+    issue_tile(0, 0, false);
     if constexpr (ADD) {
       load_mask(ks * BN, am_raw);
       if (p.kind & K_KEEP) to_additive(am_raw);
     }
-    if constexpr (CONV_V) {
-      if (hl == 0 && tid < 2) vflag[tid] = -1;
+    if constexpr (CONV_V || CONV_K) {
+      if (hl == 0 && tid < 4) vflag[tid] = -1;  // vflag[0..1], kflag[0..1]
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
     __syncthreads();
@@ -434,13 +464,27 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     const int kt0 = t * NK * BN;
     const int buf = t & 1;
     if (t + 1 < ntiles) {
-      issue_tile(kt0 + NK * BN, buf ^ 1);
+      issue_tile(kt0 + NK * BN, buf ^ 1, false);
       if constexpr (ADD) load_mask(kt0 + NK * BN + ks * BN, am_nxt);
     }
     const char* kl = smem + buf * BUF_BYTES + ks * SPLIT_BYTES;
     const char* vl = kl + TILE_BYTES;
     const char* vcl = vc_lds + (buf * NK + ks) * TILE_BYTES;
     const bool vconv = CONV_V && vflag[buf] != ((hl << 16) | t);  // f16 copy of V is usable
+    // K tiles stay bfloat16 (kbf): tile 0, which the rewrite at the end of a
+    // tile never reaches (a second rewrite site, before the loop, costs ~40
+    // registers), and a tile that did not fit float16, fetched again (the
+    // wait also covers the next tile's loads; rare)
+    bool kbf = false;
+    if constexpr (CONV_K) {
+      if (t > 0 && kflag[buf] == ((hl << 16) | t)) {
+        issue_tile(kt0, buf, true);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        kbf = true;
+      }
+      kbf |= t == 0;
+    }
     const int kb0 = kt0 + ks * BN;  // this wave's 64 keys
     bool comp = kb0 < kend_w;
     const bool edge = (kb0 + BN > kpad) || (causal && kb0 + BN - 1 > qw0);
@@ -504,15 +548,40 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       // both MFMA blocks run at raised wave priority: the SIMD's other wave
       // then fills the matrix core's gaps with its softmax arithmetic
       __builtin_amdgcn_s_setprio(1);
+      if (CONV_K && kbf) {
+        // bfloat16 K: the float16 query as two bfloat16 parts (hi + lo holds
+        // its 11 significant bits exactly)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
+        for (int cc = 0; cc < NC; ++cc) {
+          // the copy's opaque update keeps the split inside this rare branch:
+          // hoisted out of the tile loop it would hold 8 * NC more registers
+          Frag8<QT> qc = qf[cc];
+          asm volatile("" : "+v"(qc.u[0].x), "+v"(qc.u[0].y), "+v"(qc.u[0].z), "+v"(qc.u[0].w));
+          float f[8], h[8];
+          unpack8(qc, f);
+          const Frag8<T> qh = pack8<T>(f);
+          unpack8(qh, h);
 #pragma unroll
-        for (int blk = 0; blk < NB32; ++blk) {
-          Frag8<T> kf;
-          kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
-          s[blk] = mma8(kf, qf[cc], s[blk]);
-          if constexpr (PRENORM) s[blk] = mma8(kf, qlo[cc], s[blk]);
+          for (int j = 0; j < 8; ++j) f[j] -= h[j];
+          const Frag8<T> ql = pack8<T>(f);
+#pragma unroll
+          for (int blk = 0; blk < NB32; ++blk) {
+            Frag8<T> kf;
+            kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
+            s[blk] = mma8(kf, qh, s[blk]);
+            s[blk] = mma8(kf, ql, s[blk]);
+          }
         }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+          for (int blk = 0; blk < NB32; ++blk) {
+            Frag8<QT> kf;  // float16 after the rewrite (pre-LN), else the call dtype
+            kf.u[0] = lds_load16(kl + krow_off[blk] + 16 * ((2 * cc + hh) ^ ksw[blk]));
+            s[blk] = mma8(kf, qf[cc], s[blk]);
+          }
+      }
       __builtin_amdgcn_s_setprio(0);
       // online softmax over the tile [MAX 2.3]. ADD: s becomes the logit
       // scale*s + mask (natural units); otherwise s stays raw (scale > 0
@@ -666,6 +735,10 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       // passed the previous barrier.
       asm volatile("" ::: "memory");
       if (t + 1 < ntiles) convert_v(buf ^ 1, (hl << 16) | (t + 1));
+    }
+    if constexpr (CONV_K) {
+      asm volatile("" ::: "memory");
+      if (t + 1 < ntiles) convert_k(buf ^ 1, (hl << 16) | (t + 1));  // this thread's own chunks
     }
     __syncthreads();
   }

@@ -420,6 +420,26 @@ def test_graph_replays_match_eager():
         assert torch.equal(out, eager), f"replay {r}"
 
 
+@pytest.mark.parametrize("kind,D", [(0, 64), (CAUSAL, 128), (ADDITIVE, 64)])
+def test_bf16_prenorm_keys_beyond_f16_range(kind, D):
+    """Pre-LN, bfloat16: landed K tiles are rewritten into float16 for a
+    float16 Q K^T product, except tile 0 of a head, which multiplies the
+    float16 query in two exact bfloat16 parts. A tile holding a finite
+    |k| > 65504 must be fetched again and take that split product. Large
+    keys sit in tile 0, in tile 2 and (just above float16's range) in tile 3.
+    The query's float16 rounding moves a score by about 2^-12 |q_d k_d|, so
+    it stays small wherever the outlier's score is not far beyond the rest."""
+    w = W.make("bf16-big-k", "bf16", B=2, H=2, Lq=150, Lk=300, D=D, kind=kind, seed=9 + D + kind,
+               lens_range=(40, 300) if kind & ADDITIVE else None, block_p=0.1, block=16,
+               prenorm=True, x_mean=0.5, x_std=3.0, residual=True)
+    k = W.bf16_bits_to_f32(w.k).astype(np.float64)
+    k[0, 0, 10, 3] = 7.0e4           # tile 0 of (b0, h0)
+    k[0, 1, 140, 0] = -9.0e4         # tile 2 of (b0, h1)
+    k[1, 1, 200, D - 1] = 6.6e4      # tile 3 of (b1, h1), just above float16's largest value
+    w.k = W.round_to(k, "bf16")
+    _check(w, f"bf16-big-k-k{kind}-D{D}")
+
+
 @pytest.mark.parametrize("kind,D,prenorm", [(0, 64, False), (CAUSAL, 64, False), (0, 64, True),
                                             (CAUSAL | PADDING, 32, False)])
 def test_bf16_values_beyond_f16_range(kind, D, prenorm):
