@@ -206,32 +206,65 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     const int nch = F / 8;
     const int g16 = lane >> 4, l16 = lane & 15;
     float2* st = reinterpret_cast<float2*>(stat_lds) + wave * 32;
+    // A lane's chunks of one token are ch = l16, l16 + 16, ... When they fit
+    // in XC registers (F <= 128 * XC), one pass issues all their loads at once
+    // and both sums run from registers; otherwise each sum streams the row
+    // (one load in flight at a time, the row read twice).
+    constexpr int XC = 8;
     for (int r0 = 0; r0 < (ks == 0 ? 32 : 0); r0 += 4) {
       const int row = qw0 + r0 + g16;
       const bool valid = row < Lq;
       const char* xr = (const char*)p.x + ((int64_t)b * Lq + (valid ? row : 0)) * (int64_t)F * E;
       T* tag = nullptr;
-      float s = 0.f;
-      if (valid) {
-        for (int ch = l16; ch < nch; ch += 16) {
-          const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      float s = 0.f, v2 = 0.f, mean;
+      if (nch <= 16 * XC) {
+        uint4 u[XC];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s += lo_f(w[i], tag) + hi_f(w[i], tag);
+        for (int i = 0; i < XC; ++i) {
+          const int ch = l16 + 16 * i;
+          u[i] = (valid && ch < nch) ? *reinterpret_cast<const uint4*>(xr + 16 * ch)
+                                     : make_uint4(0u, 0u, 0u, 0u);  // absent chunks add 0
         }
-      }
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-      const float mean = s / (float)F;
-      float v2 = 0.f;
-      if (valid) {
-        for (int ch = l16; ch < nch; ch += 16) {
-          const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        for (int i = 0; i < XC; ++i) {
+          const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a0 = lo_f(w[i], tag) - mean, a1 = hi_f(w[i], tag) - mean;
+          for (int j = 0; j < 4; ++j) s += lo_f(w[j], tag) + hi_f(w[j], tag);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+        mean = s / (float)F;
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+          if (!(valid && l16 + 16 * i < nch)) continue;
+          const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a0 = lo_f(w[j], tag) - mean, a1 = hi_f(w[j], tag) - mean;
             v2 += a0 * a0 + a1 * a1;
+          }
+        }
+      } else {
+        if (valid) {
+          for (int ch = l16; ch < nch; ch += 16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += lo_f(w[i], tag) + hi_f(w[i], tag);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+        mean = s / (float)F;
+        if (valid) {
+          for (int ch = l16; ch < nch; ch += 16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float a0 = lo_f(w[i], tag) - mean, a1 = hi_f(w[i], tag) - mean;
+              v2 += a0 * a0 + a1 * a1;
+            }
           }
         }
       }
