@@ -207,44 +207,65 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     const int g16 = lane >> 4, l16 = lane & 15;
     float2* st = reinterpret_cast<float2*>(stat_lds) + wave * 32;
     // A lane's chunks of one token are ch = l16, l16 + 16, ... When they fit
-    // in XC registers (F <= 128 * XC), one pass issues all their loads at once
-    // and both sums run from registers; otherwise each sum streams the row
-    // (one load in flight at a time, the row read twice).
+    // in XC registers (F <= 128 * XC), the loads of two 4-token passes are
+    // issued together and both sums run from registers; otherwise each sum
+    // streams the row (one load in flight at a time, the row read twice).
     constexpr int XC = 8;
-    for (int r0 = 0; r0 < (ks == 0 ? 32 : 0); r0 += 4) {
-      const int row = qw0 + r0 + g16;
-      const bool valid = row < Lq;
-      const char* xr = (const char*)p.x + ((int64_t)b * Lq + (valid ? row : 0)) * (int64_t)F * E;
-      T* tag = nullptr;
-      float s = 0.f, v2 = 0.f, mean;
-      if (nch <= 16 * XC) {
-        uint4 u[XC];
+    const float invF = 1.0f / (float)F;
+    auto finish = [&](float s, float v2, int r) {  // s, v2: this lane's partial sums of token r
 #pragma unroll
-        for (int i = 0; i < XC; ++i) {
-          const int ch = l16 + 16 * i;
-          u[i] = (valid && ch < nch) ? *reinterpret_cast<const uint4*>(xr + 16 * ch)
-                                     : make_uint4(0u, 0u, 0u, 0u);  // absent chunks add 0
-        }
+      for (int o = 1; o < 16; o <<= 1) v2 += __shfl_xor(v2, o, 64);
+      if (l16 == 0) st[r] = make_float2(s, 1.0f / sqrtf(v2 * invF + p.eps));
+    };
+    T* tag = nullptr;
+    if (nch <= 16 * XC) {
+      for (int r0 = 0; r0 < (ks == 0 ? 32 : 0); r0 += 8) {
+        uint4 u[2][XC];
+        bool valid[2];
 #pragma unroll
-        for (int i = 0; i < XC; ++i) {
-          const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+        for (int pp = 0; pp < 2; ++pp) {
+          const int row = qw0 + r0 + 4 * pp + g16;
+          valid[pp] = row < Lq;
+          const char* xr =
+              (const char*)p.x + ((int64_t)b * Lq + (valid[pp] ? row : 0)) * (int64_t)F * E;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s += lo_f(w[j], tag) + hi_f(w[j], tag);
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-        mean = s / (float)F;
-#pragma unroll
-        for (int i = 0; i < XC; ++i) {
-          if (!(valid && l16 + 16 * i < nch)) continue;
-          const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float a0 = lo_f(w[j], tag) - mean, a1 = hi_f(w[j], tag) - mean;
-            v2 += a0 * a0 + a1 * a1;
+          for (int i = 0; i < XC; ++i) {
+            const int ch = l16 + 16 * i;
+            u[pp][i] = (valid[pp] && ch < nch) ? *reinterpret_cast<const uint4*>(xr + 16 * ch)
+                                               : make_uint4(0u, 0u, 0u, 0u);  // absent: adds 0
           }
         }
-      } else {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          float s = 0.f, v2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < XC; ++i) {
+            const uint32_t w[4] = {u[pp][i].x, u[pp][i].y, u[pp][i].z, u[pp][i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s += lo_f(w[j], tag) + hi_f(w[j], tag);
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+          const float mean = s * invF;
+#pragma unroll
+          for (int i = 0; i < XC; ++i) {
+            if (!(valid[pp] && l16 + 16 * i < nch)) continue;
+            const uint32_t w[4] = {u[pp][i].x, u[pp][i].y, u[pp][i].z, u[pp][i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float a0 = lo_f(w[j], tag) - mean, a1 = hi_f(w[j], tag) - mean;
+              v2 += a0 * a0 + a1 * a1;
+            }
+          }
+          finish(mean, v2, r0 + 4 * pp + g16);
+        }
+      }
+    } else {
+      for (int r0 = 0; r0 < (ks == 0 ? 32 : 0); r0 += 4) {
+        const int row = qw0 + r0 + g16;
+        const bool valid = row < Lq;
+        const char* xr = (const char*)p.x + ((int64_t)b * Lq + (valid ? row : 0)) * (int64_t)F * E;
+        float s = 0.f, v2 = 0.f;
         if (valid) {
           for (int ch = l16; ch < nch; ch += 16) {
             const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
@@ -255,7 +276,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-        mean = s / (float)F;
+        const float mean = s * invF;
         if (valid) {
           for (int ch = l16; ch < nch; ch += 16) {
             const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
@@ -267,11 +288,8 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
             }
           }
         }
+        finish(mean, v2, r0 + g16);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) v2 += __shfl_xor(v2, o, 64);
-      const float rstd = 1.0f / sqrtf(v2 / (float)F + p.eps);
-      if (l16 == 0) st[r0 + g16] = make_float2(mean, rstd);
     }
     __syncthreads();
     ms = st[n];
