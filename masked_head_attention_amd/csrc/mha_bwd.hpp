@@ -155,6 +155,26 @@ __device__ inline void xcd_block(int nbh, int nblk, int* bh, int* blk) {
   }
 }
 
+// Workgroup -> (head, block group) for a grid that runs in rounds (one
+// workgroup per CU). As in xcd_block, every block of a head stays on one XCD;
+// an XCD's workgroups go in block-group order, all its heads' group 0 first.
+// A CU takes the next workgroup of its XCD when its current one ends, so
+// with the longest groups first (group 0 under a causal mask, for the dkv
+// kernel) a CU that held a long group takes a short one.
+__device__ inline void xcd_lpt(int nbh, int nblk, int* bh, int* blk) {
+  const int i = blockIdx.x;
+  const int hpx = nbh / 8;  // heads per XCD among the complete groups of 8
+  const int full = hpx * 8 * nblk;
+  if (i < full) {
+    const int x = i % 8, j = i / 8;
+    *blk = j / hpx;
+    *bh = (j % hpx) * 8 + x;
+  } else {
+    *bh = i / nblk;
+    *blk = i - *bh * nblk;
+  }
+}
+
 // Entry (row, key) of the head's mask slab as float32 (0 for rows and keys
 // outside the tensor).
 template <typename T>
@@ -391,33 +411,47 @@ bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---- dK and dV per group of 4 key blocks -------------------------------------
-// Four waves, one 32-key block each (K in registers, V in LDS), share every
-// query tile through LDS: Q and dO rows and the rows' statistics are staged
-// one tile ahead as in the dq kernel. The A operands (Q and dO rows through
-// keymap) are LDS reads; the B operands of dV += P^T dO and dK += dS^T Q are
-// transposing reads of the same row-major tiles.
-// Two workgroups per CU (at most 256 registers per lane, 78 KB of LDS each at
-// D = 128). The V operand lives in the wave's own LDS tile rather than in
-// registers, so that K, both accumulators and the tile's values fit: 2
-// spilled registers at D = 128 instead of 37.
+// Eight waves, two per 32-key block (K in registers, V in an LDS tile the two
+// share). Each step stages two query tiles -- Q and dO rows and the rows'
+// statistics -- through LDS, one step ahead as in the dq kernel; the first
+// wave of a key block takes the even query tiles and the second the odd ones,
+// so a causal group's chain of tiles is half as long. At the end the two
+// waves of a block add their dK and dV through LDS, each finishing half of
+// the 32-feature blocks. The A operands (Q and dO rows through keymap) are LDS
+// reads; the B operands of dV += P^T dO and dK += dS^T Q are transposing reads
+// of the same row-major tiles.
+// One workgroup per CU (at most 256 registers per lane, 128 KB of LDS at
+// D = 128), so the grid runs in rounds; the workgroups of an XCD are dealt
+// longest first (xcd_lpt), and a CU whose long group ends early takes a short
+// one next.
 // Both MFMA blocks run at raised wave priority, as the dq kernel's dQ product.
 template <typename T, int D, bool TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dkv_kernel(const BwdParams p) {
   constexpr int FB = (D + 31) / 32;  // 32-feature blocks of the dK, dV accumulators
+  constexpr int SB = (FB + 1) / 2;   // blocks a wave hands to its partner (at most)
   constexpr int RS = tile_rs<D>();
+  constexpr int TB = 32 * RS;        // bytes of one staged 32-row tile
   constexpr int CPR = D / 8;
   constexpr int PPT = 32 * CPR;
-  constexpr int PPTH = (PPT + 255) / 256;
-  __shared__ __attribute__((aligned(16))) char qg_t[2][2][32 * RS];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float st[2][64];           // [buffer][lse x32, Delta x32]
-  __shared__ __attribute__((aligned(16))) char vt[4][32 * RS];       // each wave's V rows
+  constexpr int PPS = (2 * PPT + 511) / 512;  // pieces per thread and tensor of a step
+  // LDS during the tile loop: staged tiles [buffer][tile][Q, dO], the four
+  // blocks' V rows, row statistics [buffer][tile][lse x32, Delta x32]; after
+  // it, the partial dK, dV handed over: [wave][block][dK, dV], 4 KB each
+  constexpr int STAGE = 8 * TB, VT = 4 * TB, STATS = 2 * 128 * 4;
+  constexpr int XCH = 8 * SB * 2 * 4096;
+  constexpr int LDS = (STAGE + VT + STATS) > XCH ? (STAGE + VT + STATS) : XCH;
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  char* const stg = smem;
+  char* const vt = smem + STAGE;
+  float* const st = reinterpret_cast<float*>(smem + STAGE + VT);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int kw = wv & 3, half = wv >> 2;
   const int n = lane & 31, hh = lane >> 5;
   const int ngrp = (p.nkblk + 3) / 4;
   int bh = 0, kgp = 0;
-  xcd_block(p.B * p.H, ngrp, &bh, &kgp);
-  const int k0 = (4 * kgp + wv) * 32;  // this wave's key block
+  xcd_lpt(p.B * p.H, ngrp, &bh, &kgp);
+  const int k0 = (4 * kgp + kw) * 32;  // this wave's key block
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int kj = k0 + n;  // this lane's key (column of S)
@@ -432,14 +466,14 @@ bwd_dkv_kernel(const BwdParams p) {
 
   Frag8<T> kf[D / 16];
   load_rows<T, D>(krs, kj, hh, kf);
-  {
-    // this wave's V rows, row-major in its own LDS tile (read back by its own
-    // lanes after the barrier that precedes the tile loop)
+  if (half == 0) {
+    // the block's V rows, row-major in its LDS tile (read by both of its
+    // waves after the barrier that precedes the tile loop)
     Frag8<T> v0[D / 16];
     load_rows<T, D>(vrs, kj, hh, v0);
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb)
-      *reinterpret_cast<uint4*>(vt[wv] + n * RS + (16 * kb + 8 * hh) * 2) = v0[kb].u[0];
+      *reinterpret_cast<uint4*>(vt + kw * TB + n * RS + (16 * kb + 8 * hh) * 2) = v0[kb].u[0];
   }
   f32x16 dka[FB], dva[FB];
 #pragma unroll
@@ -447,55 +481,63 @@ bwd_dkv_kernel(const BwdParams p) {
 
   // queries before a block's first key see none of its keys (causal); a
   // block past the key length gets zeros. The group streams from its first
-  // block's first query tile; each wave computes from its own.
+  // block's first query tile (an even tile); each wave computes from its own.
   const int k0g = 4 * kgp * 32;
   const int t0 = p.causal ? k0 / 32 : 0;
   const int t0g = p.causal ? k0g / 32 : 0;
   const bool active = k0 < kend;
   const int ntile = (k0g < kend) ? (p.Lq + 31) / 32 : 0;
+  const int s0 = t0g / 2, nstep = (ntile + 1) / 2;  // step s stages tiles 2s, 2s + 1
 
-  uint4 rq[PPTH], rg[PPTH];
-  float rs = 0.f;  // thread tid < 64: lse (tid < 32) or Delta of row 32 t + tid % 32
-  auto gload = [&](int t) {
+  uint4 rq[PPS], rg[PPS];
+  float rs = 0.f;  // thread tid < 128: lse or Delta of row tid % 32 of the step's tile tid / 64
+  auto gload = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < PPTH; ++i) {
-      const int u = tid + 256 * i;
-      if (PPT % 256 == 0 || u < PPT) {
-        const uint32_t off = (uint32_t)(32 * t + u / CPR) * (D * 2) + (u % CPR) * 16;
+    for (int i = 0; i < PPS; ++i) {
+      const int u = tid + 512 * i;
+      if ((2 * PPT) % 512 == 0 || u < 2 * PPT) {
+        const int tl = u / PPT, w = u % PPT;
+        const uint32_t off = (uint32_t)(32 * (2 * s + tl) + w / CPR) * (D * 2) + (w % CPR) * 16;
         rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
         rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
       }
     }
-    if (tid < 64) {  // rows past Lq: no weight (-inf) and no Delta
-      const int row = 32 * t + (tid & 31);
-      rs = tid < 32 ? (row < p.Lq ? lse2[row] : -INFINITY) : (row < p.Lq ? dlt[row] : 0.f);
+    if (tid < 128) {  // rows past Lq: no weight (-inf) and no Delta
+      const int row = 32 * (2 * s + (tid >> 6)) + (tid & 31);
+      rs = (tid & 32) == 0 ? (row < p.Lq ? lse2[row] : -INFINITY) : (row < p.Lq ? dlt[row] : 0.f);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < PPTH; ++i) {
-      const int u = tid + 256 * i;
-      if (PPT % 256 == 0 || u < PPT) {
-        const int o = (u / CPR) * RS + (u % CPR) * 16;
-        *reinterpret_cast<uint4*>(qg_t[buf][0] + o) = rq[i];
-        *reinterpret_cast<uint4*>(qg_t[buf][1] + o) = rg[i];
+    for (int i = 0; i < PPS; ++i) {
+      const int u = tid + 512 * i;
+      if ((2 * PPT) % 512 == 0 || u < 2 * PPT) {
+        const int tl = u / PPT, w = u % PPT;
+        const int o = (buf * 2 + tl) * 2 * TB + (w / CPR) * RS + (w % CPR) * 16;
+        *reinterpret_cast<uint4*>(stg + o) = rq[i];
+        *reinterpret_cast<uint4*>(stg + o + TB) = rg[i];
       }
     }
-    if (tid < 64) st[buf][tid] = rs;
+    if (tid < 128) st[buf * 128 + tid] = rs;
   };
 
-  if (ntile > t0g) {
-    gload(t0g);
+  if (nstep > s0) {
+    gload(s0);
     lstore(0);
   }
   __syncthreads();
-  for (int t = t0g; t < ntile; ++t) {
-    const int buf = (t - t0g) & 1;
-    if (t + 1 < ntile) gload(t + 1);
-    if (active && t >= t0) {
+  for (int s = s0; s < nstep; ++s) {
+    const int buf = (s - s0) & 1;
+    if (s + 1 < nstep) gload(s + 1);
+    const int t = 2 * s + half;  // this wave's query tile
+    if (active && t >= t0 && t < ntile) {
+      const char* qt = stg + (buf * 2 + half) * 2 * TB;  // Q rows; dO rows follow
+      const char* gt = qt + TB;
+      const float* sr = st + buf * 128 + half * 64;
+      const char* vr = vt + kw * TB + n * RS + 16 * hh;
       // S = Q K^T and dP = dO V^T (Q and dO rows through keymap)
-      const char* qr = qg_t[buf][0] + keymap(n) * RS + 16 * hh;
-      const char* gr = qg_t[buf][1] + keymap(n) * RS + 16 * hh;
+      const char* qr = qt + keymap(n) * RS + 16 * hh;
+      const char* gr = gt + keymap(n) * RS + 16 * hh;
       __builtin_amdgcn_s_setprio(1);
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
@@ -504,7 +546,7 @@ bwd_dkv_kernel(const BwdParams p) {
         Frag8<T> vb;
         qa.u[0] = lds_load16(qr + 32 * kb);
         ga.u[0] = lds_load16(gr + 32 * kb);
-        vb.u[0] = lds_load16(vt[wv] + n * RS + (16 * kb + 8 * hh) * 2);
+        vb.u[0] = lds_load16(vr + 32 * kb);
         sa = mma8(qa, kf[kb], sa);
         da = mma8(ga, vb, da);
       }
@@ -513,7 +555,7 @@ bwd_dkv_kernel(const BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 32 * t + run_off(i, hh);
-        const float lrow = st[buf][run_off(i, hh)], drow = st[buf][32 + run_off(i, hh)];
+        const float lrow = sr[run_off(i, hh)], drow = sr[32 + run_off(i, hh)];
         const bool ok = kj < kend && !(p.causal && kj > row) && lrow != -INFINITY;
         if constexpr (TM) {
           const float x =
@@ -532,33 +574,77 @@ bwd_dkv_kernel(const BwdParams p) {
         split_frag<T>(ds + 8 * kk, shi, slo);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb) {
-          const Frag8<T> gb = load_tr_frag<T, D>(qg_t[buf][1], fb, kk, lane);
+          const Frag8<T> gb = load_tr_frag<T, D>(gt, fb, kk, lane);
           dva[fb] = mma8(phi, gb, dva[fb]);
           dva[fb] = mma8(plo, gb, dva[fb]);
-          const Frag8<T> qb = load_tr_frag<T, D>(qg_t[buf][0], fb, kk, lane);
+          const Frag8<T> qb = load_tr_frag<T, D>(qt, fb, kk, lane);
           dka[fb] = mma8(shi, qb, dka[fb]);
           dka[fb] = mma8(slo, qb, dka[fb]);
         }
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    if (t + 1 < ntile) lstore(buf ^ 1);  // last read at tile t - 1, before its barrier
+    if (s + 1 < nstep) lstore(buf ^ 1);  // last read at step s - 1, before its barrier
     __syncthreads();
   }
+
+  // The two waves of a block add their sums: wave half h finishes the
+  // feature blocks fb with fb % 2 == h (with one block, the first wave) and
+  // hands the others over; lane l's value of a block sits in 4 quads of 16
+  // bytes, quad q at float offset 4 (64 q + l). The staged tiles are free:
+  // every wave passed the loop's last barrier after its last read.
+  float* const xs = reinterpret_cast<float*>(smem);
+  auto slot = [&](int w, int j, int which) { return xs + ((w * SB + j) * 2 + which) * 1024; };
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb)
+    if ((fb & 1) != half) {
+      float* ok = slot(wv, fb >> 1, 0);
+      float* ov = slot(wv, fb >> 1, 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<float4*>(ok + 4 * (64 * q + lane)) =
+            make_float4(dka[fb][4 * q], dka[fb][4 * q + 1], dka[fb][4 * q + 2], dka[fb][4 * q + 3]);
+        *reinterpret_cast<float4*>(ov + 4 * (64 * q + lane)) =
+            make_float4(dva[fb][4 * q], dva[fb][4 * q + 1], dva[fb][4 * q + 2], dva[fb][4 * q + 3]);
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb)
+    if ((fb & 1) == half) {
+      const float* ik = slot(wv ^ 4, fb >> 1, 0);
+      const float* iv = slot(wv ^ 4, fb >> 1, 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = *reinterpret_cast<const float4*>(ik + 4 * (64 * q + lane));
+        const float4 b = *reinterpret_cast<const float4*>(iv + 4 * (64 * q + lane));
+        dka[fb][4 * q] += a.x;
+        dka[fb][4 * q + 1] += a.y;
+        dka[fb][4 * q + 2] += a.z;
+        dka[fb][4 * q + 3] += a.w;
+        dva[fb][4 * q] += b.x;
+        dva[fb][4 * q + 1] += b.y;
+        dva[fb][4 * q + 2] += b.z;
+        dva[fb][4 * q + 3] += b.w;
+      }
+    }
+
   // lane holds feature 32 fb + n of keys 8 (i / 4) + 4 hh + i % 4
   T* dk = static_cast<T*>(p.dk) + (int64_t)bh * p.Lk * D;
   T* dv = static_cast<T*>(p.dv) + (int64_t)bh * p.Lk * D;
   bool nonfinite = false;
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
+    if ((fb & 1) == half) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (key < p.Lk && 32 * fb + n < D) {
-        const T a = (T)(dka[fb][i] * p.scale), b = (T)dva[fb][i];
-        dk[(int64_t)key * D + 32 * fb + n] = a;
-        dv[(int64_t)key * D + 32 * fb + n] = b;
-        nonfinite |= !__builtin_isfinite((float)a) || !__builtin_isfinite((float)b);
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key < p.Lk && 32 * fb + n < D) {
+          const T a = (T)(dka[fb][i] * p.scale), b = (T)dva[fb][i];
+          dk[(int64_t)key * D + 32 * fb + n] = a;
+          dv[(int64_t)key * D + 32 * fb + n] = b;
+          nonfinite |= !__builtin_isfinite((float)a) || !__builtin_isfinite((float)b);
+        }
       }
     }
   if (__ballot(nonfinite) && lane == 0) atomicOr(p.flags, F_NONFINITE);
@@ -572,7 +658,7 @@ hipError_t launch_bwd_m(const BwdParams& p, hipStream_t stream) {
   if (gq > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(256), 0, stream, p);
   if (gk > 0)
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
