@@ -12,7 +12,8 @@
 //   Delta_i = sum_j P_ij dP_ij (the Jacobian's row term),  dQ = scale dS K,
 //   dK = scale dS^T Q.
 //
-// Two kernels, one wave per 32-row block, all contractions on 32x32x16 MFMA
+// Two kernels, two waves per 32-row block (each takes alternate tiles of the
+// other dimension and the two add their sums), all contractions on 32x32x16 MFMA
 // with float32 accumulation:
 //   * dq kernel (a query block): pass 1 computes each row's log-sum-exp from
 //     S^T = K Q^T and, with dP^T = V dO^T, Delta (a running maximum with the
@@ -130,37 +131,14 @@ __device__ inline void load_rows(const __amdgpu_buffer_rsrc_t rs, int row, int h
                    rs, (uint32_t)row * (D * 2) + (16 * kb + 8 * hh) * 2, 0, 0));
 }
 
-// Workgroup -> (head, block group). Workgroups are dealt to the 8 XCDs
-// round-robin; this map keeps every block of a head on one XCD, so the tiles
-// that all blocks of the head stream (K and V, or Q and dO) stay in that
-// XCD's L2. Heads beyond the last complete group of 8 keep the plain order.
-// An XCD's 32 CUs take its workgroups in turn, so with two per CU its
-// workgroups j and j + 32 share one; under a causal mask the work of a block
-// group grows (dq) or shrinks (dkv) with its index. A head group whose first
-// workgroup falls in an odd 32-workgroup run takes its blocks in reverse
-// order, so that a CU holding a long group also holds a short one. The order
-// is chosen per head group, so the map stays one-to-one for every shape.
-__device__ inline void xcd_block(int nbh, int nblk, int* bh, int* blk) {
-  const int i = blockIdx.x;
-  const int full = (nbh / 8) * 8 * nblk;
-  if (i < full) {
-    const int x = i % 8, j = i / 8;
-    const int hg = j / nblk;
-    *bh = hg * 8 + x;
-    *blk = j % nblk;
-    if ((hg * nblk / 32) & 1) *blk = nblk - 1 - *blk;
-  } else {
-    *bh = i / nblk;
-    *blk = i - *bh * nblk;
-  }
-}
-
 // Workgroup -> (head, block group) for a grid that runs in rounds (one
-// workgroup per CU). As in xcd_block, every block of a head stays on one XCD;
-// an XCD's workgroups go in block-group order, all its heads' group 0 first.
-// A CU takes the next workgroup of its XCD when its current one ends, so
-// with the longest groups first (group 0 under a causal mask, for the dkv
-// kernel) a CU that held a long group takes a short one.
+// workgroup per CU). Workgroups are dealt to the 8 XCDs round-robin; this map
+// keeps every block of a head on one XCD, so the tiles that all blocks of the
+// head stream (K and V, or Q and dO) stay in that XCD's L2. An XCD's
+// workgroups go in block-group order, all its heads' group 0 first, and a CU
+// takes the next one of its XCD when its current one ends: with the longest
+// groups first, a CU that held a long group takes a short one. Heads beyond
+// the last complete group of 8 keep the plain order.
 __device__ inline void xcd_lpt(int nbh, int nblk, int* bh, int* blk) {
   const int i = blockIdx.x;
   const int hpx = nbh / 8;  // heads per XCD among the complete groups of 8
@@ -205,35 +183,51 @@ __device__ inline int bwd_len(const BwdParams& p, int b, bool* bad) {
 }
 
 // ---- dQ (and the row statistics) per group of 4 query blocks --------------
-// Four waves, one 32-query block each, share every K and V tile through LDS:
-// each thread loads its 16-byte pieces of tile t + 1 into registers while the
-// waves work on tile t, and stores them into the other LDS buffer before the
-// tile's barrier. The A operands (K and V rows through keymap) are LDS reads,
-// and dQ's B operand (8 consecutive keys of one feature) is a transposing
-// read of the same row-major K tile.
-// Two workgroups per CU (at most 256 registers per lane): at D = 128 the
-// compiler fits it in 243 without spills, against 284 when left to itself.
+// Eight waves, two per 32-query block. Each step stages two K/V tiles through
+// LDS: each thread loads its 16-byte pieces of the next step's tiles into
+// registers while the waves work on the current ones, and stores them into the
+// other LDS buffer before the step's barrier. The first wave of a query block
+// takes the even key tiles and the second the odd ones, so a causal group's
+// chain of tiles is half as long; the two merge their row statistics through
+// LDS after pass 1 (in one fixed order, so both get the same values) and add
+// their dQ after pass 2, each finishing half of the 32-feature blocks. The A
+// operands (K and V rows through keymap) are LDS reads, and dQ's B operand
+// (8 consecutive keys of one feature) is a transposing read of the same
+// row-major K tile.
+// One workgroup per CU (at most 256 registers per lane: at D = 128 the
+// compiler fits it without spills), so the grid runs in rounds; the
+// workgroups of an XCD are dealt longest first (xcd_lpt).
 // The dQ product runs at raised wave priority, so the SIMD's other wave fills
 // the matrix core's gaps with its vector work (around the S and dP products,
 // which both passes share, this lost).
 template <typename T, int D, bool TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dq_kernel(const BwdParams p) {
   // 32-feature blocks of the dQ accumulators (D = 16: one block whose upper
   // 16 columns read the LDS tile's row padding and are never stored)
   constexpr int FB = (D + 31) / 32;
+  constexpr int SB = (FB + 1) / 2;  // blocks a wave hands to its partner (at most)
   constexpr int RS = tile_rs<D>();
-  constexpr int CPR = D / 8;                 // 16-byte pieces per row
-  constexpr int PPT = 32 * CPR;              // pieces per 32-row tile
-  constexpr int PPTH = (PPT + 255) / 256;    // pieces per thread (whole waves idle past PPT)
-  __shared__ __attribute__((aligned(16))) char kv[2][2][32 * RS];  // [buffer][K, V]
+  constexpr int TB = 32 * RS;       // bytes of one staged 32-row tile
+  constexpr int CPR = D / 8;        // 16-byte pieces per row
+  constexpr int PPT = 32 * CPR;     // pieces per 32-row tile
+  constexpr int PPS = (2 * PPT + 511) / 512;  // pieces per thread and tensor of a step
+  // LDS: staged tiles [buffer][tile][K, V], then each wave's row statistics
+  // (m, l, a for its 32 rows); after pass 2 the staged tiles' space holds the
+  // partial dQ handed over, [wave][block], 4 KB each
+  constexpr int STAGE = 8 * TB, XST = 8 * 32 * 3 * 4, XCH = 8 * SB * 4096;
+  constexpr int LDS = (STAGE + XST) > XCH ? (STAGE + XST) : XCH;
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  char* const stg = smem;
+  float* const xst = reinterpret_cast<float*>(smem + STAGE);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wq = wv & 3, half = wv >> 2;
   const int n = lane & 31, hh = lane >> 5;
   const int ngrp = (p.nqblk + 3) / 4;
   int bh = 0, qg = 0;
-  xcd_block(p.B * p.H, ngrp, &bh, &qg);
+  xcd_lpt(p.B * p.H, ngrp, &bh, &qg);
   if (p.causal) qg = ngrp - 1 - qg;  // the longest rows (most key tiles) first
-  const int q0 = (4 * qg + wv) * 32;  // this wave's query block
+  const int q0 = (4 * qg + wq) * 32;  // this wave's query block
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int qi = q0 + n;  // this lane's query (column of S^T)
@@ -252,17 +246,19 @@ bwd_dq_kernel(const BwdParams p) {
   const int kmax = p.causal ? min(kend, q0 + 32) : kend;
   const int ntile = q0 < p.Lq ? (kmax + 31) / 32 : 0;
   const int kmax_g = p.causal ? min(kend, 4 * qg * 32 + 128) : kend;
-  const int ntile_g = (kmax_g + 31) / 32;
+  const int nstep = ((kmax_g + 31) / 32 + 1) / 2;  // step s stages tiles 2s, 2s + 1
 
-  // staged copy of a K/V tile: piece u = tid + 256 i is row u / CPR, 16-byte
-  // chunk u % CPR; rows past the key range read as zeros
-  uint4 rk[PPTH], rv[PPTH];
-  auto gload = [&](int t) {
+  // staged copy of a step's K/V tiles: piece u = tid + 512 i is tile u / PPT,
+  // row (u % PPT) / CPR, 16-byte chunk u % CPR; rows past the key range read
+  // as zeros
+  uint4 rk[PPS], rv[PPS];
+  auto gload = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < PPTH; ++i) {
-      const int u = tid + 256 * i;
-      if (PPT % 256 == 0 || u < PPT) {
-        const uint32_t off = (uint32_t)(32 * t + u / CPR) * (D * 2) + (u % CPR) * 16;
+    for (int i = 0; i < PPS; ++i) {
+      const int u = tid + 512 * i;
+      if ((2 * PPT) % 512 == 0 || u < 2 * PPT) {
+        const int tl = u / PPT, w = u % PPT;
+        const uint32_t off = (uint32_t)(32 * (2 * s + tl) + w / CPR) * (D * 2) + (w % CPR) * 16;
         rk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
         rv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
       }
@@ -270,19 +266,22 @@ bwd_dq_kernel(const BwdParams p) {
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < PPTH; ++i) {
-      const int u = tid + 256 * i;
-      if (PPT % 256 == 0 || u < PPT) {
-        const int o = (u / CPR) * RS + (u % CPR) * 16;
-        *reinterpret_cast<uint4*>(kv[buf][0] + o) = rk[i];
-        *reinterpret_cast<uint4*>(kv[buf][1] + o) = rv[i];
+    for (int i = 0; i < PPS; ++i) {
+      const int u = tid + 512 * i;
+      if ((2 * PPT) % 512 == 0 || u < 2 * PPT) {
+        const int tl = u / PPT, w = u % PPT;
+        const int o = (buf * 2 + tl) * 2 * TB + (w / CPR) * RS + (w % CPR) * 16;
+        *reinterpret_cast<uint4*>(stg + o) = rk[i];
+        *reinterpret_cast<uint4*>(stg + o + TB) = rv[i];
       }
     }
   };
+  // this wave's K tile of the step in buffer buf (V follows it)
+  auto ktile = [&](int buf) { return stg + (buf * 2 + half) * 2 * TB; };
   // S^T and dP^T of the tile in buffer buf (K and V rows through keymap)
   auto tile = [&](int buf, f32x16& sa, f32x16& da) {
-    const char* kr = kv[buf][0] + keymap(n) * RS + 16 * hh;
-    const char* vr = kv[buf][1] + keymap(n) * RS + 16 * hh;
+    const char* kr = ktile(buf) + keymap(n) * RS + 16 * hh;
+    const char* vr = kr + TB;
     sa = f32x16{};
     da = f32x16{};
 #pragma unroll
@@ -296,18 +295,19 @@ bwd_dq_kernel(const BwdParams p) {
   };
   auto legal = [&](int key) { return key < kend && !(p.causal && key > qi); };
   // one streaming pass over the group's key tiles; body(t, buf) runs for the
-  // tiles of this wave's range
+  // tiles of this wave's share of its block's range
   auto stream = [&](auto&& body) {
-    if (ntile_g > 0) {
+    if (nstep > 0) {
       gload(0);
       lstore(0);
     }
     __syncthreads();
-    for (int t = 0; t < ntile_g; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntile_g) gload(t + 1);
+    for (int s = 0; s < nstep; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < nstep) gload(s + 1);
+      const int t = 2 * s + half;
       if (t < ntile) body(t, buf);
-      if (t + 1 < ntile_g) lstore(buf ^ 1);  // last read at tile t - 1, before its barrier
+      if (s + 1 < nstep) lstore(buf ^ 1);  // last read at step s - 1, before its barrier
       __syncthreads();
     }
   };
@@ -339,15 +339,34 @@ bwd_dq_kernel(const BwdParams p) {
     }
     m = mx;
   });
-  const float M = pair_max(m);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  const float w = exp2_fast(m - Mu);
-  const float L = pair_sum(l * w);
-  const float A = pair_sum(a * w);
-  const float lse = (L == 0.f) ? -INFINITY : Mu + __log2f(L);
-  const float delta = (L == 0.f) ? 0.f : A / L;
+  float lse, delta;
+  {
+    // this wave's keys: the two lanes of a query, then the block's other wave
+    const float M = pair_max(m);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float w = exp2_fast(m - Mu);
+    const float L = pair_sum(l * w);
+    const float A = pair_sum(a * w);
+    if (hh == 0) {
+      xst[(wv * 32 + n) * 3 + 0] = M;
+      xst[(wv * 32 + n) * 3 + 1] = L;
+      xst[(wv * 32 + n) * 3 + 2] = A;
+    }
+    __syncthreads();
+    const float* x0 = xst + (wq * 32 + n) * 3;        // the even tiles' wave
+    const float* x1 = xst + ((wq + 4) * 32 + n) * 3;  // the odd tiles'
+    const float M0 = x0[0], M1 = x1[0];
+    const float Mx = fmaxf(M0, M1);
+    const float Mxu = (Mx == -INFINITY) ? 0.f : Mx;
+    // a wave without legal keys has M = -inf and L = A = 0: its weight is 0
+    const float w0 = exp2_fast(M0 - Mxu), w1 = exp2_fast(M1 - Mxu);
+    const float Lt = x0[1] * w0 + x1[1] * w1;
+    const float At = x0[2] * w0 + x1[2] * w1;
+    lse = (Lt == 0.f) ? -INFINITY : Mxu + __log2f(Lt);
+    delta = (Lt == 0.f) ? 0.f : At / Lt;
+  }
   const bool row_ok = qi < p.Lq;
-  if (hh == 0 && row_ok) {
+  if (half == 0 && hh == 0 && row_ok) {
     p.lse2[(int64_t)bh * p.Lq + qi] = lse;
     p.delta[(int64_t)bh * p.Lq + qi] = delta;
   }
@@ -380,28 +399,61 @@ bwd_dq_kernel(const BwdParams p) {
       split_frag<T>(ds + 8 * kk, hi, lo);
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        const Frag8<T> kb = load_tr_frag<T, D>(kv[buf][0], fb, kk, lane);
+        const Frag8<T> kb = load_tr_frag<T, D>(ktile(buf), fb, kk, lane);
         dqa[fb] = mma8(hi, kb, dqa[fb]);
         dqa[fb] = mma8(lo, kb, dqa[fb]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
   });
+
+  // The two waves of a block add their sums: wave half h finishes the
+  // feature blocks fb with fb % 2 == h (with one block, the first wave) and
+  // hands the others over, lane l's values in 4 quads of 16 bytes, quad q at
+  // float offset 4 (64 q + l). The staged tiles are free: every wave passed
+  // pass 2's last barrier after its last read.
+  float* const xs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb)
+    if ((fb & 1) != half) {
+      float* o = xs + (wv * SB + (fb >> 1)) * 1024;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(o + 4 * (64 * q + lane)) =
+            make_float4(dqa[fb][4 * q], dqa[fb][4 * q + 1], dqa[fb][4 * q + 2], dqa[fb][4 * q + 3]);
+    }
+  __syncthreads();
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb)
+    if ((fb & 1) == half) {
+      const float* o = xs + ((wv ^ 4) * SB + (fb >> 1)) * 1024;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(o + 4 * (64 * q + lane));
+        dqa[fb][4 * q] += v.x;
+        dqa[fb][4 * q + 1] += v.y;
+        dqa[fb][4 * q + 2] += v.z;
+        dqa[fb][4 * q + 3] += v.w;
+      }
+    }
+
   // dQ: lane holds feature 32 fb + n of rows 8 (i / 4) + 4 hh + i % 4
   T* dq = static_cast<T*>(p.dq) + (int64_t)bh * p.Lq * D;
   bool nonfinite = false;
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
+    if ((fb & 1) == half) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (row < p.Lq && 32 * fb + n < D) {
-        const T y = (T)(dqa[fb][i] * p.scale);
-        dq[(int64_t)row * D + 32 * fb + n] = y;
-        nonfinite |= !__builtin_isfinite((float)y);
+      for (int i = 0; i < 16; ++i) {
+        const int row = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (row < p.Lq && 32 * fb + n < D) {
+          const T y = (T)(dqa[fb][i] * p.scale);
+          dq[(int64_t)row * D + 32 * fb + n] = y;
+          nonfinite |= !__builtin_isfinite((float)y);
+        }
       }
     }
-  const bool empty_row = row_ok && lse == -INFINITY;
+  const bool empty_row = half == 0 && row_ok && lse == -INFINITY;
   const uint64_t nf = __ballot(nonfinite), em = __ballot(empty_row);
   if (lane == 0) {
     const uint32_t fl = (nf ? F_NONFINITE : 0u) | (em ? F_FULLY_MASKED_ROW : 0u) |
@@ -656,7 +708,7 @@ hipError_t launch_bwd_m(const BwdParams& p, hipStream_t stream) {
   const long long gk = (long long)p.B * p.H * ((p.nkblk + 3) / 4);  // groups of 4 key blocks
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (gq > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, TM>), dim3((unsigned)gq), dim3(512), 0, stream, p);
   if (gk > 0)
     hipLaunchKernelGGL((bwd_dkv_kernel<T, D, TM>), dim3((unsigned)gk), dim3(512), 0, stream, p);
   return hipGetLastError();
