@@ -540,6 +540,7 @@ bwd_dkv_kernel(const BwdParams p) {
   const bool active = k0 < kend;
   const int ntile = (k0g < kend) ? (p.Lq + 31) / 32 : 0;
   const int s0 = t0g / 2, nstep = (ntile + 1) / 2;  // step s stages tiles 2s, 2s + 1
+  const float kbias = kj < kend ? 0.f : -INFINITY;   // this lane's key past the length
 
   uint4 rq[PPS], rg[PPS];
   float rs = 0.f;  // thread tid < 128: lse or Delta of row tid % 32 of the step's tile tid / 64
@@ -554,9 +555,14 @@ bwd_dkv_kernel(const BwdParams p) {
         rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
       }
     }
-    if (tid < 128) {  // rows past Lq: no weight (-inf) and no Delta
+    if (tid < 128) {  // rows past Lq or fully masked: no weight (+inf) and no Delta
       const int row = 32 * (2 * s + (tid >> 6)) + (tid & 31);
-      rs = (tid & 32) == 0 ? (row < p.Lq ? lse2[row] : -INFINITY) : (row < p.Lq ? dlt[row] : 0.f);
+      if ((tid & 32) == 0) {
+        const float v = row < p.Lq ? lse2[row] : INFINITY;
+        rs = v == -INFINITY ? INFINITY : v;
+      } else {
+        rs = row < p.Lq ? dlt[row] : 0.f;
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -603,27 +609,28 @@ bwd_dkv_kernel(const BwdParams p) {
         da = mma8(ga, vb, da);
       }
       __builtin_amdgcn_s_setprio(0);
-      float pr[16], ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * t + run_off(i, hh);
-        const float lrow = sr[run_off(i, hh)], drow = sr[32 + run_off(i, hh)];
-        const bool ok = kj < kend && !(p.causal && kj > row) && lrow != -INFINITY;
-        if constexpr (TM) {
-          const float x =
-              ok ? masked_logit(p, sa[i] * p.c, mask_at<T>(p, bh, row, kj)) : -INFINITY;
-          pr[i] = x != -INFINITY ? exp2_fast(x - lrow) : 0.f;
-        } else {
-          pr[i] = ok ? exp2_fast(sa[i] * p.c - lrow) : 0.f;
-        }
-        ds[i] = pr[i] * (da[i] - drow);
-      }
+      // P from the row's log-sum-exp. A row without weight holds +inf (staged
+      // so) and a key past the length adds -inf, so both give 2^-inf = 0
+      // without a per-element test; the causal test runs on the diagonal
+      // tile only. One run of 8 rows at a time: its P and dS are the A
+      // operands of one 16-row step of dV += P^T dO and dK += dS^T Q.
+      const bool diag = p.causal && t == t0;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        float pr[8], ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 16 * kk + 8 * hh + e;  // row 32 t + r
+          float x = sa[8 * kk + e] * p.c;
+          if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, 32 * t + r, kj));
+          pr[e] = exp2_fast(x - sr[r] + kbias);
+          if (diag && n > r) pr[e] = 0.f;  // key k0 + n after the row
+          ds[e] = pr[e] * (da[8 * kk + e] - sr[32 + r]);
+        }
         Frag8<T> phi, plo, shi, slo;
-        split_frag<T>(pr + 8 * kk, phi, plo);
-        split_frag<T>(ds + 8 * kk, shi, slo);
+        split_frag<T>(pr, phi, plo);
+        split_frag<T>(ds, shi, slo);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb) {
           const Frag8<T> gb = load_tr_frag<T, D>(gt, fb, kk, lane);
