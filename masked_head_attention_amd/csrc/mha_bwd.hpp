@@ -312,6 +312,10 @@ bwd_dq_kernel(const BwdParams p) {
     }
   };
 
+  // Only a tile that reaches the key length or (causal) the block's diagonal
+  // tests each key; the others are legal throughout (wave-uniform choice).
+  auto edge = [&](int t) { return 32 * t + 31 >= kend || (p.causal && 32 * t >= q0); };
+
   // pass 1: log-sum-exp (log2 units) and Delta = sum_j P_j dP_j of each row:
   // running maximum m, sum l of 2^(s - m) and sum a of 2^(s - m) dP
   float m = -INFINITY, l = 0.f, a = 0.f;
@@ -319,14 +323,21 @@ bwd_dq_kernel(const BwdParams p) {
     f32x16 sa, da;
     tile(buf, sa, da);
     float s[16], mx = m;
+    auto logits = [&](auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 32 * t + run_off(i, hh);
-      float x = sa[i] * p.c;
-      if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, qi, key));
-      s[i] = legal(key) ? x : -INFINITY;
-      mx = fmaxf(mx, s[i]);
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * t + run_off(i, hh);
+        float x = sa[i] * p.c;
+        if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, qi, key));
+        s[i] = (!EDGE || legal(key)) ? x : -INFINITY;
+        mx = fmaxf(mx, s[i]);
+      }
+    };
+    if (edge(t))
+      logits(std::true_type{});
+    else
+      logits(std::false_type{});
     const float mu = (mx == -INFINITY) ? 0.f : mx;
     const float alpha = exp2_fast(m - mu);
     l *= alpha;
@@ -375,23 +386,28 @@ bwd_dq_kernel(const BwdParams p) {
   f32x16 dqa[FB];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb) dqa[fb] = f32x16{};
+  // a row without weight (lse = -inf) subtracts +inf: 2^-inf = 0
+  const float lse_w = lse == -INFINITY ? INFINITY : lse;
   stream([&](int t, int buf) {
     f32x16 sa, da;
     tile(buf, sa, da);
     float ds[16];
+    auto grads = [&](auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 32 * t + run_off(i, hh);
-      float pr;
-      if constexpr (TM) {
-        const float x =
-            legal(key) ? masked_logit(p, sa[i] * p.c, mask_at<T>(p, bh, qi, key)) : -INFINITY;
-        pr = (x != -INFINITY && lse != -INFINITY) ? exp2_fast(x - lse) : 0.f;
-      } else {
-        pr = (legal(key) && lse != -INFINITY) ? exp2_fast(sa[i] * p.c - lse) : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * t + run_off(i, hh);
+        float x = sa[i] * p.c;
+        if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, qi, key));
+        float pr = exp2_fast(x - lse_w);
+        if constexpr (EDGE) pr = legal(key) ? pr : 0.f;
+        ds[i] = pr * (da[i] - delta);
       }
-      ds[i] = pr * (da[i] - delta);
-    }
+    };
+    if (edge(t))
+      grads(std::true_type{});
+    else
+      grads(std::false_type{});
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
