@@ -83,6 +83,27 @@ __device__ inline void split_frag(const float* x, Frag8<T>& hi, Frag8<T>& lo) {
   lo = pack8<T>(r);
 }
 
+// float16: each pair rounded in one packed conversion, then each remainder
+// x - hi (exact before its one rounding) in one mixed-precision FMA that
+// reads hi's half straight from the packed word. Left to itself the compiler
+// rounds every value a second time to feed that FMA.
+template <>
+__device__ inline void split_frag<_Float16>(const float* x, Frag8<_Float16>& hi,
+                                            Frag8<_Float16>& lo) {
+  _Float16* tag = nullptr;
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h[k] = pack2(x[2 * k], x[2 * k + 1], tag);
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(l[k]) : "v"(x[2 * k]), "v"(h[k]));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "+v"(l[k])
+        : "v"(x[2 * k + 1]), "v"(h[k]));
+  }
+  hi.u[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  lo.u[0] = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 // LDS tiles are row-major, 32 rows of D elements, RS bytes apart. The row
 // padding spreads the rows of one read over the banks; of 16, 32, 48 and 64
 // bytes, 48 measured fastest (backward workload 402.8 us; 409.6, 412.5, 447.8).
@@ -556,7 +577,7 @@ bwd_dkv_kernel(const BwdParams p) {
   const bool active = k0 < kend;
   const int ntile = (k0g < kend) ? (p.Lq + 31) / 32 : 0;
   const int s0 = t0g / 2, nstep = (ntile + 1) / 2;  // step s stages tiles 2s, 2s + 1
-  const float kbias = kj < kend ? 0.f : -INFINITY;   // this lane's key past the length
+  const bool kcut = k0 + 32 > kend;  // the block straddles the key length
 
   uint4 rq[PPS], rg[PPS];
   float rs = 0.f;  // thread tid < 128: lse or Delta of row tid % 32 of the step's tile tid / 64
@@ -626,24 +647,33 @@ bwd_dkv_kernel(const BwdParams p) {
       }
       __builtin_amdgcn_s_setprio(0);
       // P from the row's log-sum-exp. A row without weight holds +inf (staged
-      // so) and a key past the length adds -inf, so both give 2^-inf = 0
-      // without a per-element test; the causal test runs on the diagonal
-      // tile only. One run of 8 rows at a time: its P and dS are the A
-      // operands of one 16-row step of dV += P^T dO and dK += dS^T Q.
+      // so), which gives 2^-inf = 0 without a per-element test; the tests of
+      // keys past the length and of the causal diagonal run only on a tile
+      // that needs them (a wave-uniform branch). One run of 8 rows at a time:
+      // its P and dS are the A operands of one 16-row step of dV += P^T dO
+      // and dK += dS^T Q.
       const bool diag = p.causal && t == t0;
+      const bool fix = __builtin_amdgcn_readfirstlane((int)(diag || kcut)) != 0;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float pr[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int r = 16 * kk + 8 * hh + e;  // row 32 t + r
           float x = sa[8 * kk + e] * p.c;
-          if constexpr (TM) x = masked_logit(p, x, mask_at<T>(p, bh, 32 * t + r, kj));
-          pr[e] = exp2_fast(x - sr[r] + kbias);
-          if (diag && n > r) pr[e] = 0.f;  // key k0 + n after the row
-          ds[e] = pr[e] * (da[8 * kk + e] - sr[32 + r]);
+          if constexpr (TM)
+            x = masked_logit(p, x, mask_at<T>(p, bh, 32 * t + 16 * kk + 8 * hh + e, kj));
+          pr[e] = exp2_fast(x - sr[16 * kk + 8 * hh + e]);
         }
+        if (fix) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 16 * kk + 8 * hh + e;  // row 32 t + r; key k0 + n after it
+            if ((diag && n > r) || kj >= kend) pr[e] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds[e] = pr[e] * (da[8 * kk + e] - sr[32 + 16 * kk + 8 * hh + e]);
         Frag8<T> phi, plo, shi, slo;
         split_frag<T>(pr, phi, plo);
         split_frag<T>(ds, shi, slo);
