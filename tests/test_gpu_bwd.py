@@ -161,13 +161,13 @@ def test_bwd_noncausal_long_rows_sampled():
 
 @pytest.mark.parametrize("B,H,L", [(3, 15, 1024), (1, 40, 2048)])
 def test_bwd_block_map_covers_every_block(B, H, L):
-    """Both kernels map workgroups to (head, block group) with the order of
-    some head groups reversed (so that long and short causal groups share a
-    CU) and the heads past the last group of 8 in plain order. Each block's
-    gradients do not depend on which workgroup computes them, so the whole
-    call must equal one call per head bit for bit: a block computed twice or
-    never would not. One head of a reversed group is also checked against the
-    oracle."""
+    """Both kernels map workgroups to (head, block group) so that every block
+    of a head stays on one XCD and an XCD's workgroups go in block-group order
+    (longest causal groups first), with the heads past the last group of 8 in
+    plain order. Each block's gradients do not depend on which workgroup
+    computes them, so the whole call must equal one call per head bit for
+    bit: a block computed twice or never would not. One head of the mapped
+    part is also checked against the oracle."""
     import masked_head_attention_amd as M
     import torch
 
@@ -186,7 +186,7 @@ def test_bwd_block_map_covers_every_block(B, H, L):
             for name, whole, part in zip(("dq", "dk", "dv"), (gq, gk, gv), one):
                 assert np.array_equal(whole[sl], from_dev(part)), (b, h, name)
     assert M.get_flags(clear=True) == 0
-    bh = 33  # head group 4: reversed in the first shape, not in the second
+    bh = 33  # in the mapped part (complete groups of 8 heads) of both shapes
     b, h = divmod(bh, H)
     sl = (slice(b, b + 1), slice(h, h + 1))
     rq, rk, rv, _ = oracle.mha_bwd(w.f64("q")[sl], w.f64("k")[sl], w.f64("v")[sl],
