@@ -239,9 +239,9 @@ mha_status mha_decode_workspace_size(int B, int H, int Lk, int D, mha_dtype dtyp
  *   mask, mask_kind: every mask kind of mha_fwd (causal, padding lengths,
  *         additive or keep tensors, shared or PER_HEAD) with the same rules;
  *         a mask is a constant of the forward and gets no gradient.
- *   dtype: MHA_F32, MHA_F16 or MHA_BF16 (float32 runs on the vector ALUs,
- *         one wave per row; the 16-bit types on MFMA); D must be 16, 32, 64
- *         or 128.
+ *   dtype: MHA_F32, MHA_F16 or MHA_BF16 (all on MFMA, except float32 at
+ *         D = 128, which runs on the vector ALUs, one wave per row); D must be
+ *         16, 32, 64 or 128.
  *   workspace: at least mha_bwd_workspace_size(...) bytes, 16-byte aligned,
  *         owned by the caller (each row's log-sum-exp and rowsum(P * dP));
  *         no initialisation needed; overlapping calls must not share it.

@@ -15,11 +15,14 @@ static hipError_t launch_bwd_dtype(const BwdParams& p, int D, hipStream_t s) {
   }
 }
 
+// float32: the MFMA kernels of the 16-bit types (v_mfma_f32_32x32x2_f32) up to
+// D = 64; at D = 128 their tiles and fragments would not fit a CU's LDS and a
+// lane's registers, and the vector-ALU kernels run.
 static hipError_t launch_bwd_float(const BwdParams& p, int D, hipStream_t s) {
   switch (D) {
-    case 16: return launch_bwd_f32<16>(p, s);
-    case 32: return launch_bwd_f32<32>(p, s);
-    case 64: return launch_bwd_f32<64>(p, s);
+    case 16: return launch_bwd_t<float, 16>(p, s);
+    case 32: return launch_bwd_t<float, 32>(p, s);
+    case 64: return launch_bwd_t<float, 64>(p, s);
     case 128: return launch_bwd_f32<128>(p, s);
     default: return hipErrorInvalidValue;
   }

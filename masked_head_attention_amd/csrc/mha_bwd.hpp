@@ -1,6 +1,6 @@
 // mha_bwd.hpp -- backward of the fused masked multi-head attention forward for
-// gfx950 (CDNA4), float16 and bfloat16: the gradients dQ, dK, dV for an
-// upstream gradient dO.
+// gfx950 (CDNA4), float16 and bfloat16 (and float32 up to D = 64): the
+// gradients dQ, dK, dV for an upstream gradient dO.
 //
 // Source (web page, cited by title and section):
 //   [MAX] "Why attention must compute the max first" (gsyq.cn/news/340375),
@@ -37,6 +37,10 @@
 // P and dS enter the MFMAs as a pair of 16-bit values (the rounded value
 // and the rounded remainder), so the products keep about 16 significant
 // bits beyond the 16-bit type.
+// float32 runs the same kernels: a 16-element slice is 8 steps of
+// v_mfma_f32_32x32x2_f32 with the same slot assignment, fragments are 32
+// bytes, the B operands are 4-byte reads (no transposing read for 32-bit
+// elements), and P and dS enter as they are.
 #pragma once
 
 #include "mha_common.hpp"
@@ -107,8 +111,37 @@ __device__ inline void split_frag<_Float16>(const float* x, Frag8<_Float16>& hi,
 // LDS tiles are row-major, 32 rows of D elements, RS bytes apart. The row
 // padding spreads the rows of one read over the banks; of 16, 32, 48 and 64
 // bytes, 48 measured fastest (backward workload 402.8 us; 409.6, 412.5, 447.8).
-template <int D>
-constexpr int tile_rs() { return D * 2 + 48; }
+template <typename T, int D>
+constexpr int tile_rs() { return D * (int)sizeof(T) + 48; }
+
+// Eight consecutive elements (one A or B operand fragment) in LDS.
+template <typename T>
+__device__ inline Frag8<T> lds_frag(const char* p) {
+  Frag8<T> f;
+  f.u[0] = lds_load16(p);
+  if constexpr (sizeof(T) == 4) f.u[1] = lds_load16(p + 16);
+  return f;
+}
+template <typename T>
+__device__ inline void lds_put_frag(char* p, const Frag8<T>& f) {
+  *reinterpret_cast<uint4*>(p) = f.u[0];
+  if constexpr (sizeof(T) == 4) *reinterpret_cast<uint4*>(p + 16) = f.u[1];
+}
+
+// float32: the 32 x 32 product over a 16-element slice as 8 steps of
+// v_mfma_f32_32x32x2_f32. In step j a lane of half hh supplies its element j,
+// contraction index 8 hh + j: the same slot assignment as the 16-bit slice.
+__device__ inline f32x16 mma8(const Frag8<float>& a, const Frag8<float>& b, f32x16 c) {
+  const uint32_t av[8] = {a.u[0].x, a.u[0].y, a.u[0].z, a.u[0].w,
+                          a.u[1].x, a.u[1].y, a.u[1].z, a.u[1].w};
+  const uint32_t bv[8] = {b.u[0].x, b.u[0].y, b.u[0].z, b.u[0].w,
+                          b.u[1].x, b.u[1].y, b.u[1].z, b.u[1].w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[j]), __uint_as_float(bv[j]), c, 0,
+                                             0, 0);
+  return c;
+}
 
 typedef __fp16 bwd_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __bf16 bwd_bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
@@ -131,25 +164,39 @@ __device__ inline uint2 bwd_read_tr<__bf16>(const char* p) {
 // 4 j + i / 4 as its element j. Lane 4 j + c addresses row j, features
 // 4 c .. 4 c + 3 of its group's 16, so lane i gets 4 consecutive rows of
 // feature i.
+// float32 (no transposing read for 32-bit elements): eight 4-byte reads, rows
+// 16 kk + 8 (l / 32) + e of feature 32 fb + l % 32.
 template <typename T, int D>
 __device__ inline Frag8<T> load_tr_frag(const char* t, int fb, int kk, int lane) {
-  const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3;
-  const char* a = t + (16 * kk + 8 * (g >> 1) + j) * tile_rs<D>() +
-                  (32 * fb + 16 * (g & 1) + 4 * c) * 2;
-  const uint2 lo = bwd_read_tr<T>(a), hi = bwd_read_tr<T>(a + 4 * tile_rs<D>());
   Frag8<T> f;
-  f.u[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  if constexpr (sizeof(T) == 4) {
+    const char* a = t + (16 * kk + 8 * (lane >> 5)) * tile_rs<T, D>() + (32 * fb + (lane & 31)) * 4;
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const uint32_t*>(a + e * tile_rs<T, D>());
+    f.u[0] = make_uint4(v[0], v[1], v[2], v[3]);
+    f.u[1] = make_uint4(v[4], v[5], v[6], v[7]);
+  } else {
+    const int g = lane >> 4, j = (lane >> 2) & 3, c = lane & 3;
+    const char* a = t + (16 * kk + 8 * (g >> 1) + j) * tile_rs<T, D>() +
+                    (32 * fb + 16 * (g & 1) + 4 * c) * 2;
+    const uint2 lo = bwd_read_tr<T>(a), hi = bwd_read_tr<T>(a + 4 * tile_rs<T, D>());
+    f.u[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
   return f;
 }
 
 template <typename T, int D>
 __device__ inline void load_rows(const __amdgpu_buffer_rsrc_t rs, int row, int hh,
                                  Frag8<T> (&f)[D / 16]) {
+  constexpr int ES = sizeof(T);
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb)
-    f[kb].u[0] = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                   rs, (uint32_t)row * (D * 2) + (16 * kb + 8 * hh) * 2, 0, 0));
+#pragma unroll
+    for (int w = 0; w < Frag8<T>::W; ++w)
+      f[kb].u[w] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rs, (uint32_t)row * (D * ES) + (16 * kb + 8 * hh) * ES + 16 * w, 0, 0));
 }
 
 // Workgroup -> (head, block group) for a grid that runs in rounds (one
@@ -180,10 +227,14 @@ template <typename T>
 __device__ inline float mask_at(const BwdParams& p, int bh, int row, int key) {
   if (row >= p.Lq || key >= p.Lk) return 0.f;
   const int64_t slab = p.mask_heads == 1 ? bh / p.H : bh;
-  const uint16_t u =
-      static_cast<const uint16_t*>(p.mask)[(slab * p.Lq + row) * (int64_t)p.Lk + key];
-  T* tag = nullptr;
-  return lo_f((uint32_t)u, tag);
+  const int64_t at = (slab * p.Lq + row) * (int64_t)p.Lk + key;
+  if constexpr (sizeof(T) == 4) {
+    return static_cast<const float*>(p.mask)[at];
+  } else {
+    const uint16_t u = static_cast<const uint16_t*>(p.mask)[at];
+    T* tag = nullptr;
+    return lo_f((uint32_t)u, tag);
+  }
 }
 
 // A legal score in log2 units, or -inf: the mask tensor's decision and (for
@@ -228,9 +279,10 @@ bwd_dq_kernel(const BwdParams p) {
   // 16 columns read the LDS tile's row padding and are never stored)
   constexpr int FB = (D + 31) / 32;
   constexpr int SB = (FB + 1) / 2;  // blocks a wave hands to its partner (at most)
-  constexpr int RS = tile_rs<D>();
+  constexpr int ES = sizeof(T);      // element bytes
+  constexpr int RS = tile_rs<T, D>();
   constexpr int TB = 32 * RS;       // bytes of one staged 32-row tile
-  constexpr int CPR = D / 8;        // 16-byte pieces per row
+  constexpr int CPR = D * ES / 16;  // 16-byte pieces per row
   constexpr int PPT = 32 * CPR;     // pieces per 32-row tile
   constexpr int PPS = (2 * PPT + 511) / 512;  // pieces per thread and tensor of a step
   // LDS: staged tiles [buffer][tile][K, V], then each wave's row statistics
@@ -252,12 +304,12 @@ bwd_dq_kernel(const BwdParams p) {
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int qi = q0 + n;  // this lane's query (column of S^T)
-  const int64_t qoff = (int64_t)bh * p.Lq * D * 2, koff = (int64_t)bh * p.Lk * D * 2;
-  const uint32_t qbytes = (uint32_t)p.Lq * D * 2;
+  const int64_t qoff = (int64_t)bh * p.Lq * D * ES, koff = (int64_t)bh * p.Lk * D * ES;
+  const uint32_t qbytes = (uint32_t)p.Lq * D * ES;
   const auto qrs = make_rsrc(static_cast<const char*>(p.q) + qoff, qbytes);
   const auto grs = make_rsrc(static_cast<const char*>(p.dout) + qoff, qbytes);
-  const auto krs = make_rsrc(static_cast<const char*>(p.k) + koff, (uint32_t)kend * D * 2);
-  const auto vrs = make_rsrc(static_cast<const char*>(p.v) + koff, (uint32_t)kend * D * 2);
+  const auto krs = make_rsrc(static_cast<const char*>(p.k) + koff, (uint32_t)kend * D * ES);
+  const auto vrs = make_rsrc(static_cast<const char*>(p.v) + koff, (uint32_t)kend * D * ES);
 
   Frag8<T> qf[D / 16], gf[D / 16];
   load_rows<T, D>(qrs, qi, hh, qf);
@@ -279,7 +331,7 @@ bwd_dq_kernel(const BwdParams p) {
       const int u = tid + 512 * i;
       if ((2 * PPT) % 512 == 0 || u < 2 * PPT) {
         const int tl = u / PPT, w = u % PPT;
-        const uint32_t off = (uint32_t)(32 * (2 * s + tl) + w / CPR) * (D * 2) + (w % CPR) * 16;
+        const uint32_t off = (uint32_t)(32 * (2 * s + tl) + w / CPR) * (D * ES) + (w % CPR) * 16;
         rk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
         rv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
       }
@@ -301,15 +353,13 @@ bwd_dq_kernel(const BwdParams p) {
   auto ktile = [&](int buf) { return stg + (buf * 2 + half) * 2 * TB; };
   // S^T and dP^T of the tile in buffer buf (K and V rows through keymap)
   auto tile = [&](int buf, f32x16& sa, f32x16& da) {
-    const char* kr = ktile(buf) + keymap(n) * RS + 16 * hh;
+    const char* kr = ktile(buf) + keymap(n) * RS + 8 * hh * ES;
     const char* vr = kr + TB;
     sa = f32x16{};
     da = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
-      Frag8<T> kf, vf;
-      kf.u[0] = lds_load16(kr + 32 * kb);
-      vf.u[0] = lds_load16(vr + 32 * kb);
+      const Frag8<T> kf = lds_frag<T>(kr + 16 * kb * ES), vf = lds_frag<T>(vr + 16 * kb * ES);
       sa = mma8(kf, qf[kb], sa);
       da = mma8(vf, gf[kb], da);
     }
@@ -438,7 +488,7 @@ bwd_dq_kernel(const BwdParams p) {
       for (int fb = 0; fb < FB; ++fb) {
         const Frag8<T> kb = load_tr_frag<T, D>(ktile(buf), fb, kk, lane);
         dqa[fb] = mma8(hi, kb, dqa[fb]);
-        dqa[fb] = mma8(lo, kb, dqa[fb]);
+        if constexpr (ES == 2) dqa[fb] = mma8(lo, kb, dqa[fb]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -519,9 +569,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 bwd_dkv_kernel(const BwdParams p) {
   constexpr int FB = (D + 31) / 32;  // 32-feature blocks of the dK, dV accumulators
   constexpr int SB = (FB + 1) / 2;   // blocks a wave hands to its partner (at most)
-  constexpr int RS = tile_rs<D>();
+  constexpr int ES = sizeof(T);      // element bytes
+  constexpr int RS = tile_rs<T, D>();
   constexpr int TB = 32 * RS;        // bytes of one staged 32-row tile
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D * ES / 16;
   constexpr int PPT = 32 * CPR;
   constexpr int PPS = (2 * PPT + 511) / 512;  // pieces per thread and tensor of a step
   // LDS during the tile loop: staged tiles [buffer][tile][Q, dO], the four
@@ -544,12 +595,12 @@ bwd_dkv_kernel(const BwdParams p) {
   bool bad = false;
   const int kend = bwd_len(p, bh / p.H, &bad);
   const int kj = k0 + n;  // this lane's key (column of S)
-  const int64_t qoff = (int64_t)bh * p.Lq * D * 2, koff = (int64_t)bh * p.Lk * D * 2;
-  const uint32_t qbytes = (uint32_t)p.Lq * D * 2;
+  const int64_t qoff = (int64_t)bh * p.Lq * D * ES, koff = (int64_t)bh * p.Lk * D * ES;
+  const uint32_t qbytes = (uint32_t)p.Lq * D * ES;
   const auto qrs = make_rsrc(static_cast<const char*>(p.q) + qoff, qbytes);
   const auto grs = make_rsrc(static_cast<const char*>(p.dout) + qoff, qbytes);
-  const auto krs = make_rsrc(static_cast<const char*>(p.k) + koff, (uint32_t)kend * D * 2);
-  const auto vrs = make_rsrc(static_cast<const char*>(p.v) + koff, (uint32_t)kend * D * 2);
+  const auto krs = make_rsrc(static_cast<const char*>(p.k) + koff, (uint32_t)kend * D * ES);
+  const auto vrs = make_rsrc(static_cast<const char*>(p.v) + koff, (uint32_t)kend * D * ES);
   const float* lse2 = p.lse2 + (int64_t)bh * p.Lq;
   const float* dlt = p.delta + (int64_t)bh * p.Lq;
 
@@ -562,7 +613,7 @@ bwd_dkv_kernel(const BwdParams p) {
     load_rows<T, D>(vrs, kj, hh, v0);
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb)
-      *reinterpret_cast<uint4*>(vt + kw * TB + n * RS + (16 * kb + 8 * hh) * 2) = v0[kb].u[0];
+      lds_put_frag<T>(vt + kw * TB + n * RS + (16 * kb + 8 * hh) * ES, v0[kb]);
   }
   f32x16 dka[FB], dva[FB];
 #pragma unroll
@@ -587,7 +638,7 @@ bwd_dkv_kernel(const BwdParams p) {
       const int u = tid + 512 * i;
       if ((2 * PPT) % 512 == 0 || u < 2 * PPT) {
         const int tl = u / PPT, w = u % PPT;
-        const uint32_t off = (uint32_t)(32 * (2 * s + tl) + w / CPR) * (D * 2) + (w % CPR) * 16;
+        const uint32_t off = (uint32_t)(32 * (2 * s + tl) + w / CPR) * (D * ES) + (w % CPR) * 16;
         rq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
         rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0));
       }
@@ -629,19 +680,16 @@ bwd_dkv_kernel(const BwdParams p) {
       const char* qt = stg + (buf * 2 + half) * 2 * TB;  // Q rows; dO rows follow
       const char* gt = qt + TB;
       const float* sr = st + buf * 128 + half * 64;
-      const char* vr = vt + kw * TB + n * RS + 16 * hh;
+      const char* vr = vt + kw * TB + n * RS + 8 * hh * ES;
       // S = Q K^T and dP = dO V^T (Q and dO rows through keymap)
-      const char* qr = qt + keymap(n) * RS + 16 * hh;
-      const char* gr = gt + keymap(n) * RS + 16 * hh;
+      const char* qr = qt + keymap(n) * RS + 8 * hh * ES;
+      const char* gr = gt + keymap(n) * RS + 8 * hh * ES;
       __builtin_amdgcn_s_setprio(1);
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        Frag8<T> qa, ga;
-        Frag8<T> vb;
-        qa.u[0] = lds_load16(qr + 32 * kb);
-        ga.u[0] = lds_load16(gr + 32 * kb);
-        vb.u[0] = lds_load16(vr + 32 * kb);
+        const Frag8<T> qa = lds_frag<T>(qr + 16 * kb * ES), ga = lds_frag<T>(gr + 16 * kb * ES);
+        const Frag8<T> vb = lds_frag<T>(vr + 16 * kb * ES);
         sa = mma8(qa, kf[kb], sa);
         da = mma8(ga, vb, da);
       }
@@ -681,10 +729,10 @@ bwd_dkv_kernel(const BwdParams p) {
         for (int fb = 0; fb < FB; ++fb) {
           const Frag8<T> gb = load_tr_frag<T, D>(gt, fb, kk, lane);
           dva[fb] = mma8(phi, gb, dva[fb]);
-          dva[fb] = mma8(plo, gb, dva[fb]);
+          if constexpr (ES == 2) dva[fb] = mma8(plo, gb, dva[fb]);
           const Frag8<T> qb = load_tr_frag<T, D>(qt, fb, kk, lane);
           dka[fb] = mma8(shi, qb, dka[fb]);
-          dka[fb] = mma8(slo, qb, dka[fb]);
+          if constexpr (ES == 2) dka[fb] = mma8(slo, qb, dka[fb]);
         }
       }
       __builtin_amdgcn_s_setprio(0);

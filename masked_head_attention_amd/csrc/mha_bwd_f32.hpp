@@ -3,8 +3,9 @@
 // carries no gradient). Same parameters, mask rules, workspace and flags as
 // the 16-bit kernels in mha_bwd.hpp.
 //
-// CDNA4's float32 matrix rate is 1/16 of the 16-bit one, and the float32
-// workloads are short rows, so these kernels use the vector ALUs: one wave per
+// These run for D = 128, where the MFMA kernels' float32 tiles and fragments
+// do not fit a CU's LDS and a lane's registers (smaller D use the MFMA
+// kernels of mha_bwd.hpp). They use the vector ALUs: one wave per
 // query row (dQ, the row's log-sum-exp and Delta) or per key row (dK, dV),
 // four rows per workgroup. For the scores, lane l takes the keys (queries)
 // l, l + 64, ... and forms its dot products against the wave's own row, staged
