@@ -203,3 +203,32 @@ def test_bwd_f32_long_ragged_rows():
     w = W.make("bwd-f32-long", "f32", 1, 2, 517, 517, 128, kind=W.CAUSAL | W.PADDING, seed=81,
                lens_range=(200, 517))
     _check(w, "bwd-f32-long")
+
+
+BWD_KINDS = [0, W.CAUSAL, W.PADDING, W.CAUSAL | W.PADDING, W.ADDITIVE, W.ADDITIVE | W.CAUSAL,
+             W.KEEP, W.ADDITIVE | W.PER_HEAD]
+
+
+def _bwd_random_shapes(n=16, seed=4048):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        dtype = ["f32", "f16", "bf16"][c % 3]
+        D = [16, 32, 64, 128][int(rng.integers(4))]
+        kind = BWD_KINDS[int(rng.integers(len(BWD_KINDS)))]
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 11))
+        Lq, Lk = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+        cases.append((dtype, D, kind, B, H, Lq, Lk, 500 + c))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,D,kind,B,H,Lq,Lk,seed", _bwd_random_shapes())
+def test_bwd_random_shapes(dtype, D, kind, B, H, Lq, Lk, seed):
+    """Seeded random shapes for both kernels: odd tile counts (a wave pair's
+    last step with one tile), Lq != Lk (also under the causal mask), head
+    counts below and above a group of 8 (both branches of the workgroup map),
+    every element type and head size, and the mask kinds."""
+    w = W.make("bwd-rand", dtype, B, H, Lq, Lk, D, kind=kind, seed=seed,
+               lens_range=(0, Lk) if kind & (W.PADDING | W.ADDITIVE | W.KEEP) else None,
+               block_p=0.2 if kind & (W.ADDITIVE | W.KEEP) else 0.0, block=16)
+    _check(w, f"bwd-rand-{dtype}-D{D}-k{kind}-{B}x{H}x{Lq}x{Lk}")
