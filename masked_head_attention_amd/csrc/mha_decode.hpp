@@ -206,16 +206,20 @@ decode_split_kernel(const DecodeParams p) {
 #pragma unroll
   for (int f = 0; f < EPL; ++f) o[f] = 0.f;
 
+  // Every cache byte is read once per call, so the loads carry the
+  // non-temporal hint (cache-policy bit `nt`): the lines they bring in are
+  // the first to be replaced and do not push out other data.
+  constexpr int NT = 2;
   auto issue = [&](int kb, uint4 (&kr)[U], uint4 (&vr)[U]) {
     const uint32_t off0 = (uint32_t)(kb + g) * RB + sub * 16;
 #pragma unroll
     for (int u = 0; u < U; ++u)
       kr[u] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off0 + u * G * RB, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off0 + u * G * RB, 0, NT));
 #pragma unroll
     for (int u = 0; u < U; ++u)
       vr[u] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off0 + u * G * RB, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off0 + u * G * RB, 0, NT));
   };
   auto consume = [&](int kb, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
     float t[U];

@@ -112,7 +112,10 @@ __global__ __launch_bounds__(256) void softmax_rows_vec(const SoftmaxParams p) {
   for (int k = 0; k < NV; ++k) {
     const int j = lane + 64 * k;
     uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (j < nvec) u = *reinterpret_cast<const uint4*>(src + 16 * (int64_t)j);
+    // each score is read once: non-temporal loads (cache-policy bit `nt`)
+    if (j < nvec)
+      u = __builtin_bit_cast(
+          uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * (int64_t)j)));
     vec_to_f32<T>(u, x[k]);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
