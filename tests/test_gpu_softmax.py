@@ -99,18 +99,15 @@ def test_empty_calls():
     assert M.get_flags(clear=True) == 0
 
 
-def test_workload_full_size_sampled():
+def test_workload_full_size():
     """The pages' 1 x 32 x 2048 x 2048 float16 tensor, as the benchmark runs
-    it: sampled rows against the oracle, every row by properties."""
+    it: every row against the oracle, in blocks of 8192 rows."""
     w = W.softmax_config()
     got, flags = _run(w)
     assert flags == 0
-    rng = np.random.default_rng(0)
-    rows = rng.choice(w.rows, size=512, replace=False)
     flat = got.reshape(w.rows, w.cols)
     src = w.f64().reshape(w.rows, w.cols)
-    ref, _ = oracle.softmax_rows(src[rows], w.scale)
-    assert_parity(flat[rows], ref, w.dtype, "softmax-workload-sampled")
-    # every row: weights in [0, 1], sums within the float16 rounding of 2048 terms
-    assert flat.min() >= 0.0 and flat.max() <= 1.0
-    np.testing.assert_allclose(flat.sum(axis=1), 1.0, atol=2e-3)
+    for r0 in range(0, w.rows, 8192):
+        ref, rflags = oracle.softmax_rows(src[r0:r0 + 8192], w.scale)
+        assert rflags == 0
+        assert_parity(flat[r0:r0 + 8192], ref, w.dtype, f"softmax-workload-rows{r0}")
