@@ -105,24 +105,22 @@ def test_bwd_large_gradients():
     _check(w, "bwd-large", std=4.0)
 
 
-def test_bwd_workload_full_size_sampled():
+def test_bwd_workload_full_size():
     """The backward at the causal Llama-2-7B shape (the benchmark's workload),
-    in the launch configuration the benchmark times: two heads against the
-    oracle, every value finite."""
-    import torch
-
+    in the launch configuration the benchmark times: dq, dk and dv of every
+    head against the oracle, four heads at a time."""
     w = W.config(W.BWD_CONFIG)
     g = W.grad_output(w)
     gq, gk, gv, flags = _run(w, g)
     assert flags == 0
-    for h in (0, w.H - 1):
-        sl = slice(h, h + 1)
-        rq, rk, rv, _ = oracle.mha_bwd(w.f64("q")[:, sl], w.f64("k")[:, sl], w.f64("v")[:, sl],
-                                       W.to_f64(g, w.dtype)[:, sl], w.kind, None, None, w.scale)
+    q, k, v, g64 = w.f64("q"), w.f64("k"), w.f64("v"), W.to_f64(g, w.dtype)
+    for h0 in range(0, w.H, 4):
+        sl = slice(h0, h0 + 4)
+        rq, rk, rv, rflags = oracle.mha_bwd(q[:, sl], k[:, sl], v[:, sl], g64[:, sl], w.kind,
+                                            None, None, w.scale)
+        assert rflags == 0
         for name, a, b in [("dq", gq[:, sl], rq), ("dk", gk[:, sl], rk), ("dv", gv[:, sl], rv)]:
-            assert_parity(a, b, w.dtype, f"bwd-workload head {h} {name}")
-    assert np.isfinite(gq).all() and np.isfinite(gk).all() and np.isfinite(gv).all()
-    del torch
+            assert_parity(a, b, w.dtype, f"bwd-workload heads {h0}-{h0 + 3} {name}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
