@@ -144,6 +144,39 @@ mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, co
                                  float eps, const void* residual, int B, int H, int Lq, int Lk,
                                  int D, float scale, mha_dtype dtype, void* stream, void* out);
 
+/* mha_prenorm_cross_fwd with a caller-owned workspace [LNXA answer steps
+ * 1-4; mixed precision per its knowledge points]. Same arguments, results
+ * and status codes, plus:
+ *   workspace        device memory of at least
+ *                    mha_prenorm_cross_workspace_size(B,H,Lk,D,dtype) bytes,
+ *                    16-byte aligned, owned by the caller; its contents need
+ *                    no initialisation and are overwritten.
+ *   workspace_bytes  its size.
+ * For bfloat16 calls without a mask tensor (ADDITIVE or KEEP) and with
+ * Lk > 0 the call enqueues three kernels: one writes float16 copies of k and
+ * v into the workspace (nearest-even rounding, the values the attention
+ * kernel otherwise rewrites tile by tile in LDS) and, per quarter of each
+ * head, whether any value exceeds 65504 in magnitude; then the attention
+ * kernel runs on the copies for the heads without such a value, and on k, v
+ * themselves for the others. Every other call ignores the workspace and runs
+ * as mha_prenorm_cross_fwd. A missing, misaligned or short workspace where
+ * one is needed is MHA_E_WORKSPACE. Calls that overlap in time must not share
+ * a workspace. */
+mha_status mha_prenorm_cross_fwd_ws(const void* x, const void* k, const void* v, const void* mask,
+                                    unsigned mask_kind, const void* gamma, const void* beta,
+                                    float eps, const void* residual, int B, int H, int Lq, int Lk,
+                                    int D, float scale, mha_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* out);
+
+/* Workspace bytes mha_prenorm_cross_fwd_ws needs for these sizes: 0 unless
+ * dtype is bfloat16 and B, H, Lk > 0; then two float16 copies of a
+ * [B,H,Lk,D] tensor and B*H*4 int32 flags, each part rounded up to 256
+ * bytes. Pure host computation; MHA_E_NULL, MHA_E_DTYPE, MHA_E_SHAPE,
+ * MHA_E_UNSUPPORTED or MHA_E_OVERFLOW as mha_prenorm_cross_fwd. No passage:
+ * the pages' kernels take no workspace. */
+mha_status mha_prenorm_cross_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
+                                            size_t* bytes);
+
 /* The device error flag [LNXA knowledge points: a global flag the kernel
  * raises when the softmax goes bad, read back by the host]. Synchronise
  * stream, then copy the current device's flag word to *flags; clear != 0

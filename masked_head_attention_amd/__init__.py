@@ -99,9 +99,21 @@ def fwd(q, k, v, mask=None, kind: int = MASK_NONE, scale: Optional[float] = None
     return out
 
 
+def prenorm_cross_workspace_size(B: int, H: int, Lk: int, D: int, dtype: int) -> int:
+    """Bytes of workspace prenorm_cross_fwd(..., workspace=...) needs (0 unless bfloat16)."""
+    n = ctypes.c_size_t(0)
+    check(lib().mha_prenorm_cross_workspace_size(B, H, Lk, D, dtype, ctypes.byref(n)),
+          "mha_prenorm_cross_workspace_size")
+    return int(n.value)
+
+
 def prenorm_cross_fwd(x, k, v, gamma, beta, eps: float = 1e-5, residual=None, mask=None,
-                      kind: int = MASK_NONE, scale: Optional[float] = None, out=None, stream=None):
-    """Pre-LN cross-attention + residual. x [B,Lq,H*D], k/v [B,H,Lk,D] -> out [B,Lq,H*D]."""
+                      kind: int = MASK_NONE, scale: Optional[float] = None, out=None, stream=None,
+                      workspace=None):
+    """Pre-LN cross-attention + residual. x [B,Lq,H*D], k/v [B,H,Lk,D] -> out [B,Lq,H*D].
+    ``workspace`` (a uint8 GPU tensor of prenorm_cross_workspace_size(...) bytes)
+    selects mha_prenorm_cross_fwd_ws: bfloat16 K and V are copied to float16
+    once per call instead of tile by tile inside the attention kernel."""
     torch = _torch()
     _dev(x, "x")
     B, Lq, F = x.shape
@@ -118,10 +130,18 @@ def prenorm_cross_fwd(x, k, v, gamma, beta, eps: float = 1e-5, residual=None, ma
         out = torch.empty_like(x)
     _dev(out, "out", x.dtype, (B, Lq, F))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    st = lib().mha_prenorm_cross_fwd(_ptr(x), _ptr(k), _ptr(v), _ptr(m), kind, _ptr(gamma),
-                                     _ptr(beta), float(eps), _ptr(residual), B, H, Lq, Lk, D,
-                                     scale, _dtype_code(x), _stream(stream), _ptr(out))
-    check(st, "mha_prenorm_cross_fwd")
+    if workspace is None:
+        st = lib().mha_prenorm_cross_fwd(_ptr(x), _ptr(k), _ptr(v), _ptr(m), kind, _ptr(gamma),
+                                         _ptr(beta), float(eps), _ptr(residual), B, H, Lq, Lk, D,
+                                         scale, _dtype_code(x), _stream(stream), _ptr(out))
+        check(st, "mha_prenorm_cross_fwd")
+        return out
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib().mha_prenorm_cross_fwd_ws(_ptr(x), _ptr(k), _ptr(v), _ptr(m), kind, _ptr(gamma),
+                                        _ptr(beta), float(eps), _ptr(residual), B, H, Lq, Lk, D,
+                                        scale, _dtype_code(x), _ptr(workspace), workspace.numel(),
+                                        _stream(stream), _ptr(out))
+    check(st, "mha_prenorm_cross_fwd_ws")
     return out
 
 

@@ -120,7 +120,20 @@ struct Call {
   void* stream;
   void* out;
   bool prenorm;
+  bool with_ws = false;      // mha_prenorm_cross_fwd_ws
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
 };
+
+// Workspace of mha_prenorm_cross_fwd_ws: float16 copies of K and V, then the
+// copy kernel's flags, each part 256-byte aligned. Zero where the call does
+// not use one (every dtype but bfloat16, no keys).
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t prenorm_ws_bytes(int B, int H, int Lk, int D, mha_dtype dtype) {
+  if (dtype != MHA_BF16 || B == 0 || H == 0 || Lk == 0) return 0;
+  const size_t kv = (size_t)B * H * Lk * D * 2;
+  return 2 * align256(kv) + align256((size_t)B * H * mha::kKvCopySub * 4);
+}
 
 mha_status validate(const Call& c) {
   if (c.dtype != MHA_F32 && c.dtype != MHA_F16 && c.dtype != MHA_BF16) return MHA_E_DTYPE;
@@ -170,6 +183,10 @@ mha_status run(const Call& c) {
   mha_status st = validate(c);
   if (st != MHA_OK) return st;
   if (c.B == 0 || c.H == 0 || c.Lq == 0) return MHA_OK;
+  if (c.with_ws && (c.kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP)) == 0) {
+    const size_t need = prenorm_ws_bytes(c.B, c.H, c.Lk, c.D, c.dtype);
+    if (need > 0 && (!c.ws || !aligned(c.ws, 16) || c.ws_bytes < need)) return MHA_E_WORKSPACE;
+  }
   uint32_t* flags = nullptr;
   st = device_flags(&flags);
   if (st != MHA_OK) return st;
@@ -198,6 +215,12 @@ mha_status run(const Call& c) {
   const bool add = (c.kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP)) != 0;  // a mask tensor
   hipStream_t s = static_cast<hipStream_t>(c.stream);
   hipError_t e;
+  if (c.with_ws && c.dtype == MHA_BF16 && !add && c.Lk > 0) {
+    const size_t kv = align256((size_t)c.B * c.H * c.Lk * c.D * 2);
+    char* w = static_cast<char*>(c.ws);
+    e = mha::launch_bf16_prenorm_kv16(p, c.D, w, w + kv, reinterpret_cast<int*>(w + 2 * kv), s);
+    return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
+  }
   if (c.dtype == MHA_F32) e = mha::launch_f32(p, c.D, add, c.prenorm, s);
   else if (c.dtype == MHA_F16) e = mha::launch_f16(p, c.D, add, c.prenorm, s);
   else e = mha::launch_bf16(p, c.D, add, c.prenorm, s);
@@ -431,6 +454,30 @@ mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, co
   Call c{nullptr, x, k, v, mask, mask_kind, gamma, beta, eps, residual,
          B, H, Lq, Lk, D, scale, dtype, stream, out, true};
   return run(c);
+}
+
+mha_status mha_prenorm_cross_fwd_ws(const void* x, const void* k, const void* v, const void* mask,
+                                    unsigned mask_kind, const void* gamma, const void* beta,
+                                    float eps, const void* residual, int B, int H, int Lq, int Lk,
+                                    int D, float scale, mha_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* out) {
+  Call c{nullptr, x, k, v, mask, mask_kind, gamma, beta, eps, residual,
+         B, H, Lq, Lk, D, scale, dtype, stream, out, true};
+  c.with_ws = true;
+  c.ws = workspace;
+  c.ws_bytes = workspace_bytes;
+  return run(c);
+}
+
+mha_status mha_prenorm_cross_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
+                                            size_t* bytes) {
+  if (!bytes) return MHA_E_NULL;
+  if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
+  if (B < 0 || H < 0 || Lk < 0) return MHA_E_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
+  if (!count_ok({B, H, Lk, D}, 2)) return MHA_E_OVERFLOW;
+  *bytes = prenorm_ws_bytes(B, H, Lk, D, dtype);
+  return MHA_OK;
 }
 
 mha_status mha_softmax_rows(const void* s, void* p, int64_t rows, int cols, float scale,

@@ -6,4 +6,8 @@ hipError_t launch_bf16(const Params& p, int D, bool add, bool pre, hipStream_t s
   return launch_dtype<__bf16>(p, D, add, pre, s);
 }
 void tile_shape_bf16(int D, int* bm, int* rows, int* keys) { tile_shape<__bf16>(D, bm, rows, keys); }
+hipError_t launch_bf16_prenorm_kv16(const Params& p, int D, void* k16, void* v16, int* flags,
+                                    hipStream_t s) {
+  return launch_prenorm_kv16_d(p, D, k16, v16, flags, s);
+}
 }  // namespace mha

@@ -86,6 +86,65 @@ __device__ inline int swz_v16(int row) {
   else return 0;
 }
 
+// Float16 copies of K and V for bfloat16 pre-LN calls (a workspace): the
+// copy kernel below writes them with one flag per sub-range of a head, and
+// the attention kernel runs twice over the same grid.
+//   mode 0: no copies (every other call);
+//   mode 1: p.k and p.v are the float16 copies (KV16 instantiation): the
+//           launch serves the heads whose flags are all clear;
+//   mode 2: p.k and p.v are the bfloat16 tensors: the launch serves the heads
+//           with a flag set, rewriting tiles in LDS as without a workspace.
+// flags[(b*H + h)*nsub + s] != 0: sub-range s of head (b, h) holds a value of
+// magnitude above 65504, which float16 cannot hold.
+struct KvPre {
+  const int* flags;
+  int nsub;
+  int mode;
+};
+
+struct KvConvParams {
+  const void* k;   // [B,H,Lk,D] bfloat16
+  const void* v;
+  void* k16;       // [B,H,Lk,D] float16
+  void* v16;
+  int* flags;      // [B*H, nsub]
+  int64_t n16;     // 16-byte chunks of one head's K (or V): Lk*D/8
+  int nsub;        // workgroups per head
+};
+
+// One workgroup per sub-range of a head's K and V: bfloat16 -> float32 ->
+// float16 (nearest even: the rewrite the attention kernel applies to its LDS
+// tiles, so both give the same float16 values). Sources are read once, with
+// the non-temporal hint; the copies are read next by the attention kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void mha_half_kernel_kv16_copy(const KvConvParams c) {
+  const int64_t bh = blockIdx.x / c.nsub;
+  const int s = (int)(blockIdx.x % c.nsub);
+  const int64_t lo = c.n16 * s / c.nsub, hi = c.n16 * (s + 1) / c.nsub;
+  bool big = false;
+  T* tb = nullptr;
+  _Float16* th = nullptr;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const char* src = static_cast<const char*>(m ? c.v : c.k) + bh * c.n16 * 16;
+    char* dst = static_cast<char*>(m ? c.v16 : c.k16) + bh * c.n16 * 16;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * i));
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      uint32_t r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = lo_f(w[j], tb), b = hi_f(w[j], tb);
+        big |= fmaxf(fabsf(a), fabsf(b)) > 65504.f;
+        r[j] = pack2(a, b, th);
+      }
+      *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+  }
+  const int any = __syncthreads_or(big ? 1 : 0);
+  if (threadIdx.x == 0) c.flags[blockIdx.x] = any ? 1 : 0;
+}
+
 // NK = 1: 4 waves, each 32 query rows against every key tile.
 // NK = 2 (causal masks): 8 waves, two per query group, taking alternate key
 // tiles; the heaviest query block's serial chain halves and one workgroup
@@ -95,10 +154,13 @@ __device__ inline int swz_v16(int row) {
 // 16-byte vectors), 2 any other row length (read element by element). The
 // two read paths are separate instantiations so that the element-wise one's
 // scalar loads and waits never enter the vector kernel's schedule.
-template <typename T, int D, int AM, bool PRENORM, int NK>
-__global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p) {
+// KV16: the float16 copies of a bfloat16 pre-LN call (mode 1 above).
+template <typename T, int D, int AM, bool PRENORM, int NK, bool KV16 = false>
+__global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p, const KvPre kp) {
   static_assert(sizeof(T) == 2, "16-bit element types only");
   static_assert(AM >= 0 && AM <= 2, "mask form");
+  static_assert(!KV16 || (PRENORM && AM == 0 && std::is_same<T, __bf16>::value),
+                "float16 K/V copies serve bfloat16 pre-LN calls without a mask tensor");
   constexpr bool ADD = AM != 0;
   constexpr int E = 2;
   constexpr int NQ = 4, NW = NQ * NK, NT = 64 * NW, BM = 128, BN = 64, NB32 = 2;
@@ -128,7 +190,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   // A tile holding a larger finite value falls back to the split. Only where
   // the extra LDS keeps the occupancy (2 workgroups per CU for NK = 1).
   constexpr int VC_BYTES = 2 * NK * TILE_BYTES;
-  constexpr bool CONV_V = SPLIT_P && (TILE_REGION + VC_BYTES + STAT_BYTES + 16) <= (NK == 1 ? 80 : 160) * 1024;
+  constexpr bool CONV_V = SPLIT_P && !KV16 && (TILE_REGION + VC_BYTES + STAT_BYTES + 16) <= (NK == 1 ? 80 : 160) * 1024;
   constexpr float LOG2E = 1.4426950408889634f;
   constexpr float RESCALE_GAP = 8.0f;         // log2 units
   constexpr bool LS = PRENORM;                // scores leave the MFMAs in log2 units, less m
@@ -138,7 +200,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   // features. A tile holding a finite |k| > 65504 is re-loaded as bfloat16
   // and multiplied by the same float16 query split exactly into two
   // bfloat16 parts.
-  constexpr bool CONV_K = PRENORM && SPLIT_P;
+  constexpr bool CONV_K = PRENORM && SPLIT_P && !KV16;
   using QT = std::conditional_t<PRENORM, _Float16, T>;  // type of the Q fragments
   static_assert(NCHUNK % 64 == 0, "tile chunks must fill whole waves");
 
@@ -175,6 +237,19 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     }
     b = grp / ngrp;
     hg = grp % ngrp;
+  }
+  // the heads of the group this launch serves (bit hl), from the copy flags
+  const int nheads = PRENORM ? p.hg : 1;
+  unsigned serve = (1u << nheads) - 1u;
+  if (kp.mode != 0) {
+    serve = 0u;
+    for (int hl = 0; hl < nheads; ++hl) {
+      const int* f = kp.flags + ((int64_t)b * p.H + (PRENORM ? hg * p.hg + hl : hg)) * kp.nsub;
+      int any = 0;
+      for (int s2 = 0; s2 < kp.nsub; ++s2) any |= f[s2];
+      if ((any != 0) == (kp.mode == 2)) serve |= 1u << hl;
+    }
+    if (serve == 0u) return;  // the other launch serves every head of the group
   }
   const int Lq = p.Lq, Lk = p.Lk, H = p.H;
   const int q0 = qblk * BM;
@@ -310,8 +385,9 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
   const int vkey0 = 8 * (vG >> 1) + vj;
   const int vfeat0 = 16 * (vG & 1) + 8 * (vr & 1) + 4 * (vr >> 1);
 
-  const int nheads = PRENORM ? p.hg : 1;
   for (int hl = 0; hl < nheads; ++hl) {
+  if (!((serve >> hl) & 1u)) continue;
+  const bool first_head = (serve & ((1u << hl) - 1u)) == 0u;  // no earlier head served
   const int h = PRENORM ? hg * p.hg + hl : hg;
   const int64_t bh = (int64_t)b * H + h;
 
@@ -501,7 +577,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       if (p.kind & K_KEEP) to_additive(am_raw);
     }
     if constexpr (CONV_V || CONV_K) {
-      if (hl == 0 && tid < 4) vflag[tid] = -1;  // vflag[0..1], kflag[0..1]
+      if (first_head && tid < 4) vflag[tid] = -1;  // vflag[0..1], kflag[0..1]
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
     __syncthreads();
@@ -520,7 +596,7 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
     }
     const char* kl = smem + buf * BUF_BYTES + ks * SPLIT_BYTES;
     const char* vl = kl + TILE_BYTES;
-    const char* vcl = vc_lds + (buf * NK + ks) * TILE_BYTES;
+    const char* vcl = KV16 ? vl : vc_lds + (buf * NK + ks) * TILE_BYTES;  // float16 V
     const bool vconv = CONV_V && vflag[buf] != ((hl << 16) | t);  // f16 copy of V is usable
     // K tiles stay bfloat16 (kbf): tile 0, which the rewrite at the end of a
     // tile never reaches (a second rewrite site, before the loop, costs ~40
@@ -762,9 +838,10 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p)
       ++ncomp;
       using TT = std::true_type;
       using FF = std::false_type;
-      if (CONV_V && vconv) {
-        if (edge) tile(TT{}, std::integral_constant<bool, CONV_V>{});
-        else tile(FF{}, std::integral_constant<bool, CONV_V>{});
+      constexpr bool VF16 = CONV_V || KV16;  // a float16 V tile exists
+      if (KV16 || (CONV_V && vconv)) {
+        if (edge) tile(TT{}, std::integral_constant<bool, VF16>{});
+        else tile(FF{}, std::integral_constant<bool, VF16>{});
       } else {
         if (edge) tile(TT{}, FF{});
         else tile(FF{}, FF{});

@@ -18,15 +18,52 @@ template <typename T, int D>
 constexpr int skip_keys() { return sizeof(T) == 2 ? 64 : F32Cfg<D>::SUB; }
 
 // 16-bit types: 8 waves with two key splits under a causal mask, else 4
-template <typename T, int D, int AM, bool PRE>
-hipError_t launch_half(const Params& p, long long grid, hipStream_t stream) {
+template <typename T, int D, int AM, bool PRE, bool KV16 = false>
+hipError_t launch_half(const Params& p, long long grid, hipStream_t stream,
+                       KvPre kp = KvPre{nullptr, 0, 0}) {
   if (p.kind & K_CAUSAL)
-    hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 2>), dim3((unsigned)grid), dim3(512), 0,
-                       stream, p);
+    hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 2, KV16>), dim3((unsigned)grid), dim3(512),
+                       0, stream, p, kp);
   else
-    hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 1>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 1, KV16>), dim3((unsigned)grid), dim3(256),
+                       0, stream, p, kp);
   return hipGetLastError();
+}
+
+// Workgroups per head of the float16 copy kernel.
+constexpr int kKvCopySub = 4;
+
+// bfloat16 pre-LN without a mask tensor, with a workspace: the float16 copy
+// kernel, then the attention kernel on the copies (the heads whose flags are
+// clear), then on the bfloat16 tensors (the heads with a flag set). k16, v16:
+// [B,H,Lk,D] float16; flags: [B*H*kKvCopySub] int32.
+template <int D>
+hipError_t launch_prenorm_kv16(Params p, void* k16, void* v16, int* flags, hipStream_t stream) {
+  p.nqblk = (p.Lq + block_rows<__bf16, D>() - 1) / block_rows<__bf16, D>();
+  p.hg = p.H % 4 == 0 ? 4 : (p.H % 2 == 0 ? 2 : 1);
+  const long long grid = (long long)p.B * (p.H / p.hg) * p.nqblk;
+  const long long ncopy = (long long)p.B * p.H * kKvCopySub;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL || ncopy > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const KvConvParams c{p.k, p.v, k16, v16, flags, (int64_t)p.Lk * D / 8, kKvCopySub};
+  hipLaunchKernelGGL(mha_half_kernel_kv16_copy<__bf16>, dim3((unsigned)ncopy), dim3(256), 0, stream, c);
+  Params pc = p;
+  pc.k = k16;
+  pc.v = v16;
+  hipError_t e = launch_half<__bf16, D, 0, true, true>(pc, grid, stream, KvPre{flags, kKvCopySub, 1});
+  if (e != hipSuccess) return e;
+  return launch_half<__bf16, D, 0, true, false>(p, grid, stream, KvPre{flags, kKvCopySub, 2});
+}
+
+inline hipError_t launch_prenorm_kv16_d(const Params& p, int D, void* k16, void* v16, int* flags,
+                                        hipStream_t s) {
+  switch (D) {
+    case 16: return launch_prenorm_kv16<16>(p, k16, v16, flags, s);
+    case 32: return launch_prenorm_kv16<32>(p, k16, v16, flags, s);
+    case 64: return launch_prenorm_kv16<64>(p, k16, v16, flags, s);
+    case 128: return launch_prenorm_kv16<128>(p, k16, v16, flags, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T, int D, bool ADD, bool PRE>
@@ -94,5 +131,7 @@ hipError_t launch_bf16(const Params& p, int D, bool add, bool pre, hipStream_t s
 void tile_shape_f32(int D, int* bm, int* rows, int* keys);
 void tile_shape_f16(int D, int* bm, int* rows, int* keys);
 void tile_shape_bf16(int D, int* bm, int* rows, int* keys);
+hipError_t launch_bf16_prenorm_kv16(const Params& p, int D, void* k16, void* v16, int* flags,
+                                    hipStream_t s);
 
 }  // namespace mha

@@ -79,8 +79,21 @@ def gpu_inputs(w: W.Workload):
     return d
 
 
-def run_gpu(w: W.Workload, inputs=None, out=None):
-    """One call of the library on workload w; returns (out tensor, flags)."""
+def prenorm_workspace(w: W.Workload):
+    """A workspace of the size mha_prenorm_cross_fwd_ws asks for, filled with a
+    byte pattern (its contents need no initialisation)."""
+    import torch
+
+    import masked_head_attention_amd as M
+
+    code = {"f32": M.F32, "f16": M.F16, "bf16": M.BF16}[w.dtype]
+    need = M.prenorm_cross_workspace_size(w.B, w.H, w.Lk, w.D, code)
+    return torch.full((max(need, 1),), 0x5A, dtype=torch.uint8, device="cuda")
+
+
+def run_gpu(w: W.Workload, inputs=None, out=None, workspace=None):
+    """One call of the library on workload w; returns (out tensor, flags).
+    A pre-LN call with ``workspace`` goes through mha_prenorm_cross_fwd_ws."""
     import masked_head_attention_amd as M
 
     d = inputs if inputs is not None else gpu_inputs(w)
@@ -88,7 +101,7 @@ def run_gpu(w: W.Workload, inputs=None, out=None):
     if w.prenorm:
         o = M.prenorm_cross_fwd(d["x"], d["k"], d["v"], d["gamma"], d["beta"], w.eps,
                                 residual=d["x"] if w.residual else None, mask=d["mask"],
-                                kind=w.kind, scale=w.scale, out=out)
+                                kind=w.kind, scale=w.scale, out=out, workspace=workspace)
     else:
         o = M.fwd(d["q"], d["k"], d["v"], mask=d["mask"], kind=w.kind, scale=w.scale, out=out)
     return o, M.get_flags(clear=True)

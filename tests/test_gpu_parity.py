@@ -12,8 +12,8 @@ import pytest
 
 import oracle
 import workloads as W
-from helpers import (TOL, assert_parity, from_dev, gpu_inputs, half_ulp, run_gpu,
-                     run_oracle, to_dev)
+from helpers import (TOL, assert_parity, from_dev, gpu_inputs, half_ulp, prenorm_workspace,
+                     run_gpu, run_oracle, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -174,15 +174,19 @@ def _nan_out(w):
     return torch.full(shape, float("nan"), dtype=torch_dtype(w.dtype), device="cuda")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_workload_full_size_elementwise(cfg):
+@pytest.mark.parametrize("cfg,ws", [(1, False), (2, False), (3, False), (4, False), (4, True),
+                                    (5, False)])
+def test_workload_full_size_elementwise(cfg, ws):
     """Every output element of the full-size workload against the fp64 oracle
     (the whole grid, including the XCD workgroup remap and the heaviest-first
     causal order). The pre-LN cross-attention workload (B=32, H=16,
-    Lq=Lk=2048, D=64, bfloat16) is compared against the unrounded oracle."""
+    Lq=Lk=2048, D=64, bfloat16) is compared against the unrounded oracle,
+    with and without a workspace (the benchmark times the workspace call)."""
     w = W.config(cfg)
-    print(f"[parity] full-size cfg{cfg} {w.name} elementwise", flush=True)
-    out_t, flags = run_gpu(w, out=_nan_out(w))
+    print(f"[parity] full-size cfg{cfg} {w.name} elementwise, workspace {ws}", flush=True)
+    wsp = prenorm_workspace(w) if ws else None
+    out_t, flags = run_gpu(w, out=_nan_out(w), workspace=wsp)
+    del wsp
     got = from_dev(out_t)
     del out_t
     ref, rflags = run_oracle(w)
