@@ -1,5 +1,6 @@
 """HIP graph capture of the calls the benchmark times as graphs: the decode
-call (split and merge kernels) and the backward (dq and dkv kernels). Each
+call (split and merge kernels), the backward (dq and dkv kernels) and the
+bfloat16 pre-LN call with a workspace (copy kernel and two attention kernels). Each
 graph is replayed several times, with eager work and synchronisations in
 between, and every replay must reproduce the eager result bit for bit (the
 calls enqueue only kernels: no memset or allocation inside the captured
@@ -82,4 +83,25 @@ def test_backward_graph_replays(dtype):
                      device="cuda")
     _replays(lambda: M.bwd(q, k, v, g, kind=w.kind, scale=w.scale, dq=dq, dk=dk, dv=dv,
                            workspace=ws), [dq, dk, dv])
+    assert M.get_flags(clear=True) == 0
+
+
+def test_prenorm_workspace_graph_replays():
+    """Both attention launches serve heads (one head holds a value beyond
+    float16's range); the workspace is zeroed between replays, so every replay
+    must rewrite the copies and the flags it reads."""
+    import masked_head_attention_amd as M
+    import torch
+
+    w = W.make("graph-prenorm-ws", "bf16", 2, 4, 150, 300, 64, seed=52, prenorm=True,
+               x_mean=0.5, x_std=3.0, residual=True)
+    v = W.bf16_bits_to_f32(w.v).astype(np.float64)
+    v[1, 2, 77, 5] = 1.0e5
+    w.v = W.round_to(v, "bf16")
+    x, k, v2, gm, bt = (to_dev(getattr(w, n), w.dtype) for n in ("x", "k", "v", "gamma", "beta"))
+    out = torch.empty_like(x)
+    ws = torch.empty(M.prenorm_cross_workspace_size(w.B, w.H, w.Lk, w.D, M.BF16),
+                     dtype=torch.uint8, device="cuda")
+    _replays(lambda: M.prenorm_cross_fwd(x, k, v2, gm, bt, w.eps, residual=x, scale=w.scale,
+                                         out=out, workspace=ws), [out, ws])
     assert M.get_flags(clear=True) == 0
