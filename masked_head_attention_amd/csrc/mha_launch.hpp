@@ -55,17 +55,6 @@ hipError_t launch_prenorm_kv16(Params p, void* k16, void* v16, int* flags, hipSt
   return launch_half<__bf16, D, 0, true, false>(p, grid, stream, KvPre{flags, kKvCopySub, 2});
 }
 
-inline hipError_t launch_prenorm_kv16_d(const Params& p, int D, void* k16, void* v16, int* flags,
-                                        hipStream_t s) {
-  switch (D) {
-    case 16: return launch_prenorm_kv16<16>(p, k16, v16, flags, s);
-    case 32: return launch_prenorm_kv16<32>(p, k16, v16, flags, s);
-    case 64: return launch_prenorm_kv16<64>(p, k16, v16, flags, s);
-    case 128: return launch_prenorm_kv16<128>(p, k16, v16, flags, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 template <typename T, int D, bool ADD, bool PRE>
 hipError_t launch_one(Params p, hipStream_t stream) {
   p.nqblk = (p.Lq + block_rows<T, D>() - 1) / block_rows<T, D>();
