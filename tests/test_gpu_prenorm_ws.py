@@ -149,3 +149,21 @@ def test_ws_reuse_is_deterministic():
     c2, _ = run_gpu(w2, inputs=d2, workspace=prenorm_workspace(w2))
     assert torch.equal(a1, b1)
     assert torch.equal(a2, c2)
+
+
+@pytest.mark.parametrize("garbage", ["nan", "nan-inf"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_ws_nonfinite_padding_rows_do_not_leak(garbage, D):
+    """Key rows at or past a sequence's length do not take part [MMHA 3.1].
+    NaN there is copied to float16 and never read (the attention kernel's
+    buffers end at the length); an infinity flags its head, which then takes
+    the bfloat16 kernel, which never reads it either. No NONFINITE flag."""
+    w = _case(D, PADDING, B=3, H=4, Lq=90, Lk=200, seed=800 + D)
+    w.lens = np.array([37, 130, 1], np.int32)
+    for name in ("k", "v"):
+        a = w.f64(name).copy()
+        for b, L in enumerate(w.lens):
+            a[b, :, L::2] = np.nan
+            a[b, :, L + 1::2] = np.inf if garbage == "nan-inf" else np.nan
+        setattr(w, name, W.round_to(a, "bf16"))
+    _ws_vs_oracle(w, f"ws-pad-garbage-{garbage}-D{D}")
