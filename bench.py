@@ -174,7 +174,7 @@ def gpu_setup(w: W.Workload, workspace: bool = True):
     if workspace and w.prenorm and w.dtype == "bf16":
         import masked_head_attention_amd as M
 
-        need = M.prenorm_cross_workspace_size(w.B, w.H, w.Lk, w.D, M.BF16)
+        need = M.prenorm_cross_workspace_size(w.B, w.H, w.Lq, w.Lk, w.D, M.BF16)
         d["ws"] = torch.empty(need, dtype=torch.uint8, device="cuda")
     return d
 

@@ -148,17 +148,18 @@ mha_status mha_prenorm_cross_fwd(const void* x, const void* k, const void* v, co
  * 1-4; mixed precision per its knowledge points]. Same arguments, results
  * and status codes, plus:
  *   workspace        device memory of at least
- *                    mha_prenorm_cross_workspace_size(B,H,Lk,D,dtype) bytes,
+ *                    mha_prenorm_cross_workspace_size(B,H,Lq,Lk,D,dtype) bytes,
  *                    16-byte aligned, owned by the caller; its contents need
  *                    no initialisation and are overwritten.
  *   workspace_bytes  its size.
  * For bfloat16 calls without a mask tensor (ADDITIVE or KEEP) and with
  * Lk > 0 the call enqueues three kernels: one writes float16 copies of k and
  * v into the workspace (nearest-even rounding, the values the attention
- * kernel otherwise rewrites tile by tile in LDS) and, per quarter of each
- * head, whether any value exceeds 65504 in magnitude; then the attention
- * kernel runs on the copies for the heads without such a value, and on k, v
- * themselves for the others. Every other call ignores the workspace and runs
+ * kernel otherwise rewrites tile by tile in LDS), per quarter of each head
+ * whether any value exceeds 65504 in magnitude, and each token's LayerNorm
+ * mean and 1/sqrt(var + eps); then the attention kernel runs on the copies
+ * and those statistics for the heads without such a value, and on k, v and
+ * x themselves (as mha_prenorm_cross_fwd) for the others. Every other call ignores the workspace and runs
  * as mha_prenorm_cross_fwd. A missing, misaligned or short workspace where
  * one is needed is MHA_E_WORKSPACE. Calls that overlap in time must not share
  * a workspace. */
@@ -169,12 +170,12 @@ mha_status mha_prenorm_cross_fwd_ws(const void* x, const void* k, const void* v,
                                     size_t workspace_bytes, void* stream, void* out);
 
 /* Workspace bytes mha_prenorm_cross_fwd_ws needs for these sizes: 0 unless
- * dtype is bfloat16 and B, H, Lk > 0; then two float16 copies of a
- * [B,H,Lk,D] tensor and B*H*4 int32 flags, each part rounded up to 256
- * bytes. Pure host computation; MHA_E_NULL, MHA_E_DTYPE, MHA_E_SHAPE,
- * MHA_E_UNSUPPORTED or MHA_E_OVERFLOW as mha_prenorm_cross_fwd. No passage:
- * the pages' kernels take no workspace. */
-mha_status mha_prenorm_cross_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
+ * dtype is bfloat16 and B, H, Lq, Lk > 0; then two float16 copies of a
+ * [B,H,Lk,D] tensor, B*H*4 int32 flags and B*Lq float32 pairs, each part
+ * rounded up to 256 bytes. Pure host computation; MHA_E_NULL, MHA_E_DTYPE,
+ * MHA_E_SHAPE, MHA_E_UNSUPPORTED or MHA_E_OVERFLOW as mha_prenorm_cross_fwd.
+ * No passage: the pages' kernels take no workspace. */
+mha_status mha_prenorm_cross_workspace_size(int B, int H, int Lq, int Lk, int D, mha_dtype dtype,
                                             size_t* bytes);
 
 /* The device error flag [LNXA knowledge points: a global flag the kernel

@@ -99,10 +99,10 @@ def fwd(q, k, v, mask=None, kind: int = MASK_NONE, scale: Optional[float] = None
     return out
 
 
-def prenorm_cross_workspace_size(B: int, H: int, Lk: int, D: int, dtype: int) -> int:
+def prenorm_cross_workspace_size(B: int, H: int, Lq: int, Lk: int, D: int, dtype: int) -> int:
     """Bytes of workspace prenorm_cross_fwd(..., workspace=...) needs (0 unless bfloat16)."""
     n = ctypes.c_size_t(0)
-    check(lib().mha_prenorm_cross_workspace_size(B, H, Lk, D, dtype, ctypes.byref(n)),
+    check(lib().mha_prenorm_cross_workspace_size(B, H, Lq, Lk, D, dtype, ctypes.byref(n)),
           "mha_prenorm_cross_workspace_size")
     return int(n.value)
 
@@ -112,8 +112,9 @@ def prenorm_cross_fwd(x, k, v, gamma, beta, eps: float = 1e-5, residual=None, ma
                       workspace=None):
     """Pre-LN cross-attention + residual. x [B,Lq,H*D], k/v [B,H,Lk,D] -> out [B,Lq,H*D].
     ``workspace`` (a uint8 GPU tensor of prenorm_cross_workspace_size(...) bytes)
-    selects mha_prenorm_cross_fwd_ws: bfloat16 K and V are copied to float16
-    once per call instead of tile by tile inside the attention kernel."""
+    selects mha_prenorm_cross_fwd_ws: bfloat16 K and V are copied to float16,
+    and the tokens' LayerNorm statistics computed, once per call instead of
+    inside every attention workgroup."""
     torch = _torch()
     _dev(x, "x")
     B, Lq, F = x.shape

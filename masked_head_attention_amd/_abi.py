@@ -28,7 +28,8 @@ SIGNATURES = {
                                _i, _vp, _vp], _i),
     "mha_prenorm_cross_fwd_ws": ([_vp, _vp, _vp, _vp, _u, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i,
                                   _f, _i, _vp, ctypes.c_size_t, _vp, _vp], _i),
-    "mha_prenorm_cross_workspace_size": ([_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)], _i),
+    "mha_prenorm_cross_workspace_size": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
+                                         _i),
     "mha_get_flags": ([_vp, ctypes.POINTER(ctypes.c_uint32), _i], _i),
     "mha_set_debug_counters": ([_vp], _i),
     "mha_tile_config": ([_i, _i, _u, ctypes.POINTER(_i), ctypes.POINTER(_i)], _i),

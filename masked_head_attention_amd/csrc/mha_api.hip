@@ -125,14 +125,22 @@ struct Call {
   size_t ws_bytes = 0;
 };
 
-// Workspace of mha_prenorm_cross_fwd_ws: float16 copies of K and V, then the
-// copy kernel's flags, each part 256-byte aligned. Zero where the call does
-// not use one (every dtype but bfloat16, no keys).
+// Workspace of mha_prenorm_cross_fwd_ws: float16 copies of K and V, the copy
+// kernel's flags, then each token's LayerNorm statistics, each part 256-byte
+// aligned. Zero where the call does not use one (every dtype but bfloat16,
+// no queries or no keys).
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-size_t prenorm_ws_bytes(int B, int H, int Lk, int D, mha_dtype dtype) {
-  if (dtype != MHA_BF16 || B == 0 || H == 0 || Lk == 0) return 0;
-  const size_t kv = (size_t)B * H * Lk * D * 2;
-  return 2 * align256(kv) + align256((size_t)B * H * mha::kKvCopySub * 4);
+struct PrenormWs {
+  size_t kv, flags, stats, total;  // part sizes (aligned) and the sum
+};
+PrenormWs prenorm_ws(int B, int H, int Lq, int Lk, int D, mha_dtype dtype) {
+  if (dtype != MHA_BF16 || B == 0 || H == 0 || Lq == 0 || Lk == 0) return PrenormWs{0, 0, 0, 0};
+  PrenormWs w;
+  w.kv = align256((size_t)B * H * Lk * D * 2);
+  w.flags = align256((size_t)B * H * mha::kKvCopySub * 4);
+  w.stats = align256((size_t)B * Lq * 8);
+  w.total = 2 * w.kv + w.flags + w.stats;
+  return w;
 }
 
 mha_status validate(const Call& c) {
@@ -184,7 +192,7 @@ mha_status run(const Call& c) {
   if (st != MHA_OK) return st;
   if (c.B == 0 || c.H == 0 || c.Lq == 0) return MHA_OK;
   if (c.with_ws && (c.kind & (MHA_MASK_ADDITIVE | MHA_MASK_KEEP)) == 0) {
-    const size_t need = prenorm_ws_bytes(c.B, c.H, c.Lk, c.D, c.dtype);
+    const size_t need = prenorm_ws(c.B, c.H, c.Lq, c.Lk, c.D, c.dtype).total;
     if (need > 0 && (!c.ws || !aligned(c.ws, 16) || c.ws_bytes < need)) return MHA_E_WORKSPACE;
   }
   uint32_t* flags = nullptr;
@@ -216,9 +224,10 @@ mha_status run(const Call& c) {
   hipStream_t s = static_cast<hipStream_t>(c.stream);
   hipError_t e;
   if (c.with_ws && c.dtype == MHA_BF16 && !add && c.Lk > 0) {
-    const size_t kv = align256((size_t)c.B * c.H * c.Lk * c.D * 2);
+    const PrenormWs ws = prenorm_ws(c.B, c.H, c.Lq, c.Lk, c.D, c.dtype);
     char* w = static_cast<char*>(c.ws);
-    e = mha::launch_bf16_prenorm_kv16(p, c.D, w, w + kv, reinterpret_cast<int*>(w + 2 * kv), s);
+    e = mha::launch_bf16_prenorm_kv16(p, c.D, w, w + ws.kv, reinterpret_cast<int*>(w + 2 * ws.kv),
+                                      reinterpret_cast<float2*>(w + 2 * ws.kv + ws.flags), s);
     return e == hipSuccess ? MHA_OK : MHA_E_LAUNCH;
   }
   if (c.dtype == MHA_F32) e = mha::launch_f32(p, c.D, add, c.prenorm, s);
@@ -469,14 +478,14 @@ mha_status mha_prenorm_cross_fwd_ws(const void* x, const void* k, const void* v,
   return run(c);
 }
 
-mha_status mha_prenorm_cross_workspace_size(int B, int H, int Lk, int D, mha_dtype dtype,
+mha_status mha_prenorm_cross_workspace_size(int B, int H, int Lq, int Lk, int D, mha_dtype dtype,
                                             size_t* bytes) {
   if (!bytes) return MHA_E_NULL;
   if (dtype != MHA_F32 && dtype != MHA_F16 && dtype != MHA_BF16) return MHA_E_DTYPE;
-  if (B < 0 || H < 0 || Lk < 0) return MHA_E_SHAPE;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return MHA_E_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return MHA_E_UNSUPPORTED;
-  if (!count_ok({B, H, Lk, D}, 2)) return MHA_E_OVERFLOW;
-  *bytes = prenorm_ws_bytes(B, H, Lk, D, dtype);
+  if (!count_ok({B, H, Lk, D}, 2) || !count_ok({B, Lq, 8}, 1)) return MHA_E_OVERFLOW;
+  *bytes = prenorm_ws(B, H, Lq, Lk, D, dtype).total;
   return MHA_OK;
 }
 

@@ -91,7 +91,8 @@ __device__ inline int swz_v16(int row) {
 // the attention kernel runs twice over the same grid.
 //   mode 0: no copies (every other call);
 //   mode 1: p.k and p.v are the float16 copies (KV16 instantiation): the
-//           launch serves the heads whose flags are all clear;
+//           launch serves the heads whose flags are all clear, with each
+//           token's LayerNorm statistics read from `stats`;
 //   mode 2: p.k and p.v are the bfloat16 tensors: the launch serves the heads
 //           with a flag set, rewriting tiles in LDS as without a workspace.
 // flags[(b*H + h)*nsub + s] != 0: sub-range s of head (b, h) holds a value of
@@ -100,6 +101,7 @@ struct KvPre {
   const int* flags;
   int nsub;
   int mode;
+  const float2* stats;  // mode 1: [B*Lq] (mean, 1/sqrt(var + eps)) of each token
 };
 
 struct KvConvParams {
@@ -110,16 +112,100 @@ struct KvConvParams {
   int* flags;      // [B*H, nsub]
   int64_t n16;     // 16-byte chunks of one head's K (or V): Lk*D/8
   int nsub;        // workgroups per head
+  int nstat;       // workgroups computing statistics (first); the rest copy, B*H*nsub
+  const void* x;   // [B*Lq, F] bfloat16 tokens
+  float2* stats;   // [B*Lq] (mean, 1/sqrt(var + eps))
+  int64_t ntok;    // B*Lq
+  int F;           // H*D features per token
+  float eps;
 };
 
-// One workgroup per sub-range of a head's K and V: bfloat16 -> float32 ->
-// float16 (nearest even: the rewrite the attention kernel applies to its LDS
-// tiles, so both give the same float16 values). Sources are read once, with
-// the non-temporal hint; the copies are read next by the attention kernel.
+// The first nstat workgroups: the LayerNorm statistics of the tokens [LNXA
+// answer step 2], mean then mean squared deviation over the F features in
+// float32. The others: one per sub-range of a head's K and V, bfloat16 ->
+// float32 -> float16 (nearest even: the rewrite the attention kernel applies
+// to its LDS tiles, so both give the same float16 values). Sources are read
+// once, with the non-temporal hint; the copies are read next by the attention
+// kernel. The statistics come first in the grid so that their loads overlap
+// the copy's.
 template <typename T>
 __global__ __launch_bounds__(256) void mha_half_kernel_kv16_copy(const KvConvParams c) {
-  const int64_t bh = blockIdx.x / c.nsub;
-  const int s = (int)(blockIdx.x % c.nsub);
+  if ((int)blockIdx.x < c.nstat) {
+    // 16 lanes per token, 4 tokens per wave and pass; up to 128 chunks of 16
+    // bytes per token (F <= 1024) stay in registers, all loads in flight at
+    // once, and both sums run from them; longer rows are read twice
+    constexpr int XC = 8;
+    const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15;
+    const int nch = c.F / 8;
+    const float invF = 1.0f / (float)c.F;
+    T* tag = nullptr;
+    const int64_t step = (int64_t)c.nstat * 16;  // tokens per pass of the whole grid
+    for (int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4; t0 < c.ntok; t0 += step) {
+      const int64_t tok = t0 + g16;
+      const bool valid = tok < c.ntok;
+      const char* xr = static_cast<const char*>(c.x) +
+                       (valid ? tok : 0) * (int64_t)c.F * (int64_t)sizeof(T);
+      float sum = 0.f, v2 = 0.f;
+      if (nch <= 16 * XC) {
+        uint4 u[XC];
+#pragma unroll
+        for (int j = 0; j < XC; ++j) {
+          const int ch = l16 + 16 * j;
+          u[j] = (valid && ch < nch) ? *reinterpret_cast<const uint4*>(xr + 16 * ch)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < XC; ++j) {
+          const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum += lo_f(w[i], tag) + hi_f(w[i], tag);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        const float mean = sum * invF;
+#pragma unroll
+        for (int j = 0; j < XC; ++j) {
+          if (l16 + 16 * j >= nch) continue;
+          const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = lo_f(w[i], tag) - mean, a1 = hi_f(w[i], tag) - mean;
+            v2 += a0 * a0 + a1 * a1;
+          }
+        }
+        sum = mean;
+      } else {
+        for (int ch = l16; ch < nch; ch += 16) {
+          if (!valid) break;
+          const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum += lo_f(w[i], tag) + hi_f(w[i], tag);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        const float mean = sum * invF;
+        for (int ch = l16; ch < nch; ch += 16) {
+          if (!valid) break;
+          const uint4 u = *reinterpret_cast<const uint4*>(xr + 16 * ch);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a0 = lo_f(w[i], tag) - mean, a1 = hi_f(w[i], tag) - mean;
+            v2 += a0 * a0 + a1 * a1;
+          }
+        }
+        sum = mean;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v2 += __shfl_xor(v2, o, 64);
+      if (valid && l16 == 0) c.stats[tok] = make_float2(sum, 1.0f / sqrtf(v2 * invF + c.eps));
+    }
+    return;
+  }
+  const int64_t blk = (int64_t)blockIdx.x - c.nstat;  // a copy workgroup
+  const int64_t bh = blk / c.nsub;
+  const int s = (int)(blk % c.nsub);
   const int64_t lo = c.n16 * s / c.nsub, hi = c.n16 * (s + 1) / c.nsub;
   bool big = false;
   T* tb = nullptr;
@@ -142,7 +228,7 @@ __global__ __launch_bounds__(256) void mha_half_kernel_kv16_copy(const KvConvPar
     }
   }
   const int any = __syncthreads_or(big ? 1 : 0);
-  if (threadIdx.x == 0) c.flags[blockIdx.x] = any ? 1 : 0;
+  if (threadIdx.x == 0) c.flags[blk] = any ? 1 : 0;
 }
 
 // NK = 1: 4 waves, each 32 query rows against every key tile.
@@ -274,7 +360,10 @@ __global__ __launch_bounds__((256 * NK), 2) void mha_half_kernel(const Params p,
 
   // ---- pre-LN: token statistics, once per workgroup for all its heads ----
   float2 ms = make_float2(0.f, 0.f);
-  if constexpr (PRENORM) {
+  if constexpr (KV16) {
+    // statistics computed by the copy kernel
+    if (row_ok) ms = kp.stats[(int64_t)b * Lq + qi];
+  } else if constexpr (PRENORM) {
     // token statistics over F = H*D features [LNXA answer step 2]: 16 lanes per
     // token, 4 tokens per pass, mean then mean squared deviation
     const int F = H * D;

@@ -20,7 +20,7 @@ constexpr int skip_keys() { return sizeof(T) == 2 ? 64 : F32Cfg<D>::SUB; }
 // 16-bit types: 8 waves with two key splits under a causal mask, else 4
 template <typename T, int D, int AM, bool PRE, bool KV16 = false>
 hipError_t launch_half(const Params& p, long long grid, hipStream_t stream,
-                       KvPre kp = KvPre{nullptr, 0, 0}) {
+                       KvPre kp = KvPre{nullptr, 0, 0, nullptr}) {
   if (p.kind & K_CAUSAL)
     hipLaunchKernelGGL((mha_half_kernel<T, D, AM, PRE, 2, KV16>), dim3((unsigned)grid), dim3(512),
                        0, stream, p, kp);
@@ -33,26 +33,34 @@ hipError_t launch_half(const Params& p, long long grid, hipStream_t stream,
 // Workgroups per head of the float16 copy kernel.
 constexpr int kKvCopySub = 4;
 
-// bfloat16 pre-LN without a mask tensor, with a workspace: the float16 copy
-// kernel, then the attention kernel on the copies (the heads whose flags are
-// clear), then on the bfloat16 tensors (the heads with a flag set). k16, v16:
-// [B,H,Lk,D] float16; flags: [B*H*kKvCopySub] int32.
+// bfloat16 pre-LN without a mask tensor, with a workspace: the copy kernel
+// (float16 K and V, and every token's LayerNorm statistics), then the
+// attention kernel on the copies (the heads whose flags are clear), then on
+// the bfloat16 tensors (the heads with a flag set). k16, v16: [B,H,Lk,D]
+// float16; flags: [B*H*kKvCopySub] int32; stats: [B*Lq] float2.
 template <int D>
-hipError_t launch_prenorm_kv16(Params p, void* k16, void* v16, int* flags, hipStream_t stream) {
+hipError_t launch_prenorm_kv16(Params p, void* k16, void* v16, int* flags, float2* stats,
+                               hipStream_t stream) {
   p.nqblk = (p.Lq + block_rows<__bf16, D>() - 1) / block_rows<__bf16, D>();
   p.hg = p.H % 4 == 0 ? 4 : (p.H % 2 == 0 ? 2 : 1);
   const long long grid = (long long)p.B * (p.H / p.hg) * p.nqblk;
   const long long ncopy = (long long)p.B * p.H * kKvCopySub;
+  const long long ntok = (long long)p.B * p.Lq;
+  const long long nstat = std::min((ntok + 15) / 16, 2048LL);  // 16 tokens per workgroup pass
   if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL || ncopy > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const KvConvParams c{p.k, p.v, k16, v16, flags, (int64_t)p.Lk * D / 8, kKvCopySub};
-  hipLaunchKernelGGL(mha_half_kernel_kv16_copy<__bf16>, dim3((unsigned)ncopy), dim3(256), 0, stream, c);
+  if (grid > 0x7fffffffLL || ncopy + nstat > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const KvConvParams c{p.k, p.v, k16, v16, flags, (int64_t)p.Lk * D / 8, kKvCopySub, (int)nstat,
+                       p.x, stats, (int64_t)ntok, p.H * D, p.eps};
+  hipLaunchKernelGGL(mha_half_kernel_kv16_copy<__bf16>, dim3((unsigned)(ncopy + nstat)), dim3(256),
+                     0, stream, c);
   Params pc = p;
   pc.k = k16;
   pc.v = v16;
-  hipError_t e = launch_half<__bf16, D, 0, true, true>(pc, grid, stream, KvPre{flags, kKvCopySub, 1});
+  hipError_t e = launch_half<__bf16, D, 0, true, true>(pc, grid, stream,
+                                                       KvPre{flags, kKvCopySub, 1, stats});
   if (e != hipSuccess) return e;
-  return launch_half<__bf16, D, 0, true, false>(p, grid, stream, KvPre{flags, kKvCopySub, 2});
+  return launch_half<__bf16, D, 0, true, false>(p, grid, stream,
+                                                KvPre{flags, kKvCopySub, 2, nullptr});
 }
 
 template <typename T, int D, bool ADD, bool PRE>
@@ -121,6 +129,6 @@ void tile_shape_f32(int D, int* bm, int* rows, int* keys);
 void tile_shape_f16(int D, int* bm, int* rows, int* keys);
 void tile_shape_bf16(int D, int* bm, int* rows, int* keys);
 hipError_t launch_bf16_prenorm_kv16(const Params& p, int D, void* k16, void* v16, int* flags,
-                                    hipStream_t s);
+                                    float2* stats, hipStream_t s);
 
 }  // namespace mha

@@ -87,7 +87,7 @@ def prenorm_workspace(w: W.Workload):
     import masked_head_attention_amd as M
 
     code = {"f32": M.F32, "f16": M.F16, "bf16": M.BF16}[w.dtype]
-    need = M.prenorm_cross_workspace_size(w.B, w.H, w.Lk, w.D, code)
+    need = M.prenorm_cross_workspace_size(w.B, w.H, w.Lq, w.Lk, w.D, code)
     return torch.full((max(need, 1),), 0x5A, dtype=torch.uint8, device="cuda")
 
 

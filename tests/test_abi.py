@@ -299,27 +299,31 @@ def _pre_ws(workspace=A, workspace_bytes=1 << 40, x=A, k=A, v=A, mask=None, kind
         workspace, workspace_bytes, None, out)]
 
 
-def _pre_ws_size(B, H, Lk, D, dtype=2):
+def _pre_ws_size(B, H, Lq, Lk, D, dtype=2):
     n = ctypes.c_size_t(0)
-    st = _abi.lib().mha_prenorm_cross_workspace_size(B, H, Lk, D, dtype, ctypes.byref(n))
+    st = _abi.lib().mha_prenorm_cross_workspace_size(B, H, Lq, Lk, D, dtype, ctypes.byref(n))
     return _abi.STATUS[st], n.value
 
 
 def test_prenorm_workspace_size():
-    """bfloat16: two float16 copies of [B,H,Lk,D] and B*H*4 int32 flags, each
-    part rounded up to 256 bytes; every other dtype, or no keys, needs none."""
+    """bfloat16: two float16 copies of [B,H,Lk,D], B*H*4 int32 flags and B*Lq
+    float32 pairs, each part rounded up to 256 bytes; every other dtype, or no
+    queries or keys, needs none."""
     kv = (2 * 16 * 2048 * 64 * 2 + 255) // 256 * 256
-    assert _pre_ws_size(2, 16, 2048, 64) == ("MHA_OK", 2 * kv + (2 * 16 * 16 + 255) // 256 * 256)
-    assert _pre_ws_size(1, 1, 3, 16) == ("MHA_OK", 2 * 256 + 256)
-    assert _pre_ws_size(2, 16, 2048, 64, dtype=1) == ("MHA_OK", 0)
-    assert _pre_ws_size(2, 16, 2048, 64, dtype=0) == ("MHA_OK", 0)
-    assert _pre_ws_size(2, 16, 0, 64) == ("MHA_OK", 0)
-    assert _pre_ws_size(0, 16, 2048, 64) == ("MHA_OK", 0)
-    assert _pre_ws_size(1, 1, 10, 48)[0] == "MHA_E_UNSUPPORTED"
-    assert _pre_ws_size(1, 1, 10, 64, dtype=9)[0] == "MHA_E_DTYPE"
-    assert _pre_ws_size(1, -1, 10, 64)[0] == "MHA_E_SHAPE"
-    assert _pre_ws_size(1 << 30, 1 << 30, 1 << 20, 64)[0] == "MHA_E_OVERFLOW"
-    assert _abi.lib().mha_prenorm_cross_workspace_size(1, 1, 1, 64, 2, None) == \
+    assert _pre_ws_size(2, 16, 2048, 2048, 64) == (
+        "MHA_OK", 2 * kv + (2 * 16 * 16 + 255) // 256 * 256 + 2 * 2048 * 8)
+    assert _pre_ws_size(1, 1, 5, 3, 16) == ("MHA_OK", 2 * 256 + 256 + 256)
+    assert _pre_ws_size(2, 16, 2048, 2048, 64, dtype=1) == ("MHA_OK", 0)
+    assert _pre_ws_size(2, 16, 2048, 2048, 64, dtype=0) == ("MHA_OK", 0)
+    assert _pre_ws_size(2, 16, 2048, 0, 64) == ("MHA_OK", 0)
+    assert _pre_ws_size(2, 16, 0, 2048, 64) == ("MHA_OK", 0)
+    assert _pre_ws_size(0, 16, 2048, 2048, 64) == ("MHA_OK", 0)
+    assert _pre_ws_size(1, 1, 10, 10, 48)[0] == "MHA_E_UNSUPPORTED"
+    assert _pre_ws_size(1, 1, 10, 10, 64, dtype=9)[0] == "MHA_E_DTYPE"
+    assert _pre_ws_size(1, -1, 10, 10, 64)[0] == "MHA_E_SHAPE"
+    assert _pre_ws_size(1, 1, -10, 10, 64)[0] == "MHA_E_SHAPE"
+    assert _pre_ws_size(1 << 30, 1 << 30, 4, 1 << 20, 64)[0] == "MHA_E_OVERFLOW"
+    assert _abi.lib().mha_prenorm_cross_workspace_size(1, 1, 1, 1, 64, 2, None) == \
         _abi.STATUS_CODE["MHA_E_NULL"]
 
 
@@ -331,11 +335,11 @@ def test_prenorm_workspace_size():
     # bfloat16 without a mask tensor needs the workspace
     (dict(workspace=None), "MHA_E_WORKSPACE"),
     (dict(workspace=A + 8), "MHA_E_WORKSPACE"),
-    (dict(workspace_bytes=2303), "MHA_E_WORKSPACE"),
+    (dict(workspace_bytes=2559), "MHA_E_WORKSPACE"),
     # empty calls succeed without touching a device or the workspace
     (dict(Lq=0, workspace=None), "MHA_OK"),
     (dict(B=0, workspace=None), "MHA_OK"),
 ])
 def test_prenorm_ws_validation(kw, status):
-    assert _pre_ws_size(1, 2, 4, 64)[1] == 2304  # the size the short-workspace case misses by one
+    assert _pre_ws_size(1, 2, 4, 4, 64)[1] == 2560  # the size the short-workspace case misses by one
     assert _pre_ws(**kw) == status

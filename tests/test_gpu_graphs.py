@@ -100,7 +100,9 @@ def test_prenorm_workspace_graph_replays():
     w.v = W.round_to(v, "bf16")
     x, k, v2, gm, bt = (to_dev(getattr(w, n), w.dtype) for n in ("x", "k", "v", "gamma", "beta"))
     out = torch.empty_like(x)
-    ws = torch.empty(M.prenorm_cross_workspace_size(w.B, w.H, w.Lk, w.D, M.BF16),
+    # zeros: the alignment padding between the workspace's parts is never
+    # written, and the replays below compare the whole buffer
+    ws = torch.zeros(M.prenorm_cross_workspace_size(w.B, w.H, w.Lq, w.Lk, w.D, M.BF16),
                      dtype=torch.uint8, device="cuda")
     _replays(lambda: M.prenorm_cross_fwd(x, k, v2, gm, bt, w.eps, residual=x, scale=w.scale,
                                          out=out, workspace=ws), [out, ws])

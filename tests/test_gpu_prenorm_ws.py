@@ -104,15 +104,15 @@ def test_ws_sizes_errors_and_ignored_workspaces():
 
     import masked_head_attention_amd as M
 
-    B, H, Lk, D = 2, 4, 300, 64
-    need = M.prenorm_cross_workspace_size(B, H, Lk, D, M.BF16)
+    B, H, Lq, Lk, D = 2, 4, 150, 300, 64
+    need = M.prenorm_cross_workspace_size(B, H, Lq, Lk, D, M.BF16)
     kv = (B * H * Lk * D * 2 + 255) // 256 * 256
-    assert need == 2 * kv + (B * H * 16 + 255) // 256 * 256
-    assert M.prenorm_cross_workspace_size(B, H, Lk, D, M.F16) == 0
-    assert M.prenorm_cross_workspace_size(B, H, Lk, D, M.F32) == 0
-    assert M.prenorm_cross_workspace_size(B, H, 0, D, M.BF16) == 0
+    assert need == 2 * kv + (B * H * 16 + 255) // 256 * 256 + (B * Lq * 8 + 255) // 256 * 256
+    assert M.prenorm_cross_workspace_size(B, H, Lq, Lk, D, M.F16) == 0
+    assert M.prenorm_cross_workspace_size(B, H, Lq, Lk, D, M.F32) == 0
+    assert M.prenorm_cross_workspace_size(B, H, Lq, 0, D, M.BF16) == 0
 
-    w = _case(D, 0, B=B, H=H, Lk=Lk, seed=600)
+    w = _case(D, 0, B=B, H=H, Lq=Lq, Lk=Lk, seed=600)
     d = gpu_inputs(w)
     short = torch.zeros(need - 1, dtype=torch.uint8, device="cuda")
     with pytest.raises(M.MhaError) as e:
