@@ -167,3 +167,24 @@ def test_ws_nonfinite_padding_rows_do_not_leak(garbage, D):
             a[b, :, L + 1::2] = np.inf if garbage == "nan-inf" else np.nan
         setattr(w, name, W.round_to(a, "bf16"))
     _ws_vs_oracle(w, f"ws-pad-garbage-{garbage}-D{D}")
+
+
+def _ws_random_cases(n=10, seed=4242):
+    rng = np.random.default_rng(seed)
+    kinds = [0, CAUSAL, PADDING, CAUSAL | PADDING]
+    out = []
+    for i in range(n):
+        out.append((int(rng.choice([16, 32, 64, 128])), int(rng.choice(kinds)),
+                    int(rng.integers(1, 4)), int(rng.integers(1, 9)), int(rng.integers(1, 300)),
+                    int(rng.integers(1, 300)), 900 + i))
+    return out
+
+
+@pytest.mark.parametrize("D,kind,B,H,Lq,Lk,seed", _ws_random_cases())
+def test_ws_random_shapes(D, kind, B, H, Lq, Lk, seed):
+    """Seeded random shapes: head groups of 1, 2 and 4, ragged query and key
+    counts (one key to several tiles), every mask kind the copies serve."""
+    w = W.make("prenorm-ws-rand", "bf16", B=B, H=H, Lq=Lq, Lk=Lk, D=D, kind=kind, seed=seed,
+               lens_range=(0, Lk) if kind & PADDING else None, prenorm=True, x_mean=0.5,
+               x_std=3.0, residual=True)
+    _ws_vs_oracle(w, f"ws-rand-{seed}")
