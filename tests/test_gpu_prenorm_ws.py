@@ -96,6 +96,17 @@ def test_ws_heads_beyond_float16(D, kind):
         assert np.array_equal(got[b, :, cols], plain[b, :, cols]), (b, h)
 
 
+@pytest.mark.parametrize("D,kind,Lk", [(64, PADDING, 384), (128, 0, 257), (32, PADDING, 500),
+                                       (64, CAUSAL | PADDING, 512)])
+def test_ws_remapped_grids(D, kind, Lk):
+    """Grids of 32 workgroups (B=4, two groups of 4 heads, 4 query blocks):
+    without a causal mask a grid that is a multiple of 8 takes the remap that
+    keeps a head group's query blocks on one XCD, so each workgroup's batch
+    entry, head group and length come from the remapped index."""
+    w = _case(D, kind, H=8, B=4, Lq=512, Lk=Lk, seed=1000 + D + kind)
+    _ws_vs_oracle(w, f"ws-grid32-D{D}-k{kind}-Lk{Lk}")
+
+
 def test_ws_sizes_errors_and_ignored_workspaces():
     """The size query, a short or misaligned workspace (MHA_E_WORKSPACE), and
     calls that ignore the workspace (float16, a mask tensor): those equal the
