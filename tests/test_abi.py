@@ -20,6 +20,20 @@ def _declared():
     return sorted(set(re.findall(r"\b(mha_[a-z_]+)\s*\(", src)))
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the binding raises: no call has a fallback."""
+    import masked_head_attention_amd as M
+
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "libmha.so"))
+    with pytest.raises(ImportError, match="missing"):
+        _abi.lib()
+    with pytest.raises(ImportError, match="missing"):
+        M.init()
+    with pytest.raises(ImportError, match="missing"):
+        M.prenorm_cross_workspace_size(2, 4, 8, 8, 64, M.BF16)
+
+
 def test_exports_every_declared_symbol():
     lib = _abi.lib()
     names = _declared()
